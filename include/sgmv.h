@@ -1,0 +1,153 @@
+/*
+ * sgmv.h -- C ABI of libsgmv.so, SGMV (segmented gather matrix-vector
+ * multiplication) for multi-LoRA serving on AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  A LoRA-adapted linear layer outputs the base product plus
+ * a low-rank correction, y = xW + xAB, with A of shape [H1, r] and B of shape
+ * [r, H2] (Punica walkthrough, omica.com.cn/news/959180, section 2.1).  A
+ * batch mixes requests for many adapters; the correction for request i,
+ * x_i A_i B_i, is computed in two steps: the shrink v_i = x_i A_i, a gather of
+ * the request's A out of one back-to-back stack of all adapters' A matrices
+ * followed by a vector-matrix product, and the expand v_i B_i over the
+ * likewise stacked B matrices (same page, section 2.2; aivaro.ru answer 959,
+ * section 3.2).  Requests for the same adapter form contiguous row segments
+ * (segmented inputs and outputs: Punica review on nubint.ai, "Proposed
+ * method").  This library adds the correction, times a scale s, to y:
+ *
+ *     for every segment t, every row i in [seg_indptr[t], seg_indptr[t+1]):
+ *         a = adapter_ids[t]
+ *         v[i, :] = x[i, :] @ A_stack[a]                  (shrink, H1 -> r)
+ *         y[i, :] = y[i, :] + s * v[i, :] @ B_stack[a]    (expand, r -> H2)
+ *
+ * Layout (all row-major, dense, no padding):
+ *     x        [num_rows, H1]              dtype
+ *     y        [num_rows, H2]              dtype, updated in place
+ *     A_stack  [num_adapters, H1, r]       dtype, adapter a at a*H1*r
+ *     B_stack  [num_adapters, r, H2]       dtype, adapter a at a*r*H2
+ *     v        [num_rows, r]               float32 (the shrink output)
+ *     seg_indptr  int32 [num_segments + 1], non-decreasing, CSR row pointer
+ *     adapter_ids int32 [num_segments]
+ * x, A_stack, B_stack and y share one dtype; every sum is accumulated in
+ * float32 and y is rounded once (nearest-even) to its dtype.
+ *
+ * Pointers.  Every array argument is a DEVICE pointer owned by the caller
+ * (the host-side validator is the one exception and says so).  The library
+ * keeps no state between calls, allocates no memory and never synchronises
+ * the host with the device: each call only enqueues kernels on `stream`
+ * (a hipStream_t; NULL means the default stream) and returns.
+ *
+ * Segment table.  Rows outside every segment are left untouched; empty
+ * segments do nothing; an adapter may name several segments; segments must
+ * not overlap.  The table is read on the device and is not validated on the
+ * host (that would need a device-to-host copy).  For memory safety the
+ * kernels clamp segment bounds to [0, num_rows) and skip a segment whose
+ * adapter id lies outside [0, num_adapters); what a malformed table computes
+ * is otherwise unspecified.  sgmv_validate_segments() checks a host copy.
+ *
+ * Aliasing.  y must not overlap x, v, the stacks or the workspace.
+ *
+ * Errors.  Calls return SGMV_OK after enqueueing, or a status describing the
+ * first problem found by the host-side checks (made before anything is
+ * enqueued) or by the HIP launch.  Device faults surface at the caller's
+ * next synchronisation, as usual for HIP.  num_rows == 0 or
+ * num_segments == 0 is a valid no-op.
+ *
+ * Rank.  r is a runtime argument (any 1 <= r <= SGMV_MAX_RANK, no
+ * recompilation: aivaro.ru answer 959, section 3.2).  Ranks 8, 16, 32, 64
+ * and 128 (and 4 for float32) with 16-byte aligned arrays take the
+ * vectorised kernels; anything else takes a slower general kernel that
+ * computes the same thing.
+ */
+#ifndef SGMV_H
+#define SGMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SGMV_ABI_VERSION 1
+#define SGMV_MAX_RANK 128
+
+typedef enum {
+    SGMV_F32 = 0,
+    SGMV_F16 = 1,
+    SGMV_BF16 = 2
+} sgmv_dtype_t;
+
+typedef enum {
+    SGMV_OK = 0,
+    SGMV_ERR_NULL_PTR = 1,     /* a required pointer is NULL                    */
+    SGMV_ERR_BAD_SHAPE = 2,    /* negative size, r outside [1, SGMV_MAX_RANK]   */
+    SGMV_ERR_BAD_DTYPE = 3,    /* dtype is not one of sgmv_dtype_t              */
+    SGMV_ERR_UNSUPPORTED = 4,  /* sizes beyond what the kernels index (>2^31)   */
+    SGMV_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than required       */
+    SGMV_ERR_HIP = 6,          /* a HIP launch reported an error                */
+    SGMV_ERR_BAD_SEGMENTS = 7  /* (validator only) malformed segment table      */
+} sgmv_status_t;
+
+/* Version of this ABI (SGMV_ABI_VERSION of the library that was loaded). */
+int sgmv_abi_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* sgmv_status_string(int status);
+
+/*
+ * Shrink: v[i, :] = x[i, :] @ A_stack[adapter_ids[t]] for every row i of
+ * every segment t (overwrite; float32).  Rows of v outside every segment
+ * keep their contents.  The reduction over H1 is split across workgroups and
+ * combined in a fixed order, so repeated calls give identical bits.
+ *
+ * workspace: device scratch of at least sgmv_shrink_workspace_bytes(...)
+ * bytes (any contents; overwritten).  May be NULL only when that size is 0.
+ */
+size_t sgmv_shrink_workspace_bytes(int32_t num_rows, int32_t num_segments,
+                                   int32_t H1, int32_t r, int32_t dtype);
+int sgmv_shrink(float* v, const void* x, const void* A_stack,
+                const int32_t* seg_indptr, const int32_t* adapter_ids,
+                int32_t num_segments, int32_t num_rows, int32_t num_adapters,
+                int32_t H1, int32_t r, int32_t dtype,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Expand: y[i, :] = round(y[i, :] + scale * (v[i, :] @ B_stack[adapter_ids[t]]))
+ * for every row i of every segment t; v is float32 [num_rows, r], the sum
+ * over r is taken in float32 and y is rounded once to its dtype.
+ */
+int sgmv_expand(void* y, const float* v, const void* B_stack,
+                const int32_t* seg_indptr, const int32_t* adapter_ids,
+                int32_t num_segments, int32_t num_rows, int32_t num_adapters,
+                int32_t r, int32_t H2, float scale, int32_t dtype, void* stream);
+
+/*
+ * Fused add-on: y[i, :] = round(y[i, :] + scale * (x[i, :] @ A_a) @ B_a),
+ * a = adapter_ids of row i's segment.  The intermediate v stays in float32
+ * and never leaves the workspace.
+ *
+ * workspace: device scratch of at least lora_apply_workspace_bytes(...)
+ * bytes (any contents; overwritten).
+ */
+size_t lora_apply_workspace_bytes(int32_t num_rows, int32_t num_segments,
+                                  int32_t H1, int32_t H2, int32_t r, int32_t dtype);
+int lora_apply(void* y, const void* x, const void* A_stack, const void* B_stack,
+               const int32_t* seg_indptr, const int32_t* adapter_ids,
+               int32_t num_segments, int32_t num_rows, int32_t num_adapters,
+               int32_t H1, int32_t H2, int32_t r, float scale, int32_t dtype,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Host-side check of a segment table held in HOST memory: seg_indptr
+ * non-decreasing from >= 0, seg_indptr[num_segments] <= num_rows, every
+ * adapter id in [0, num_adapters).  Returns SGMV_OK or SGMV_ERR_BAD_SEGMENTS
+ * (SGMV_ERR_NULL_PTR / SGMV_ERR_BAD_SHAPE for bad arguments).
+ */
+int sgmv_validate_segments(const int32_t* h_seg_indptr, const int32_t* h_adapter_ids,
+                           int32_t num_segments, int32_t num_rows, int32_t num_adapters);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGMV_H */

@@ -1,0 +1,244 @@
+"""SGMV for MI355X: multi-LoRA shrink/expand as hand-written HIP kernels.
+
+Thin Python binding over the C ABI of ``libsgmv.so`` (declared in
+``include/sgmv.h``).  The functions here only check and marshal torch
+tensors (dtype, device, shape, contiguity), pick up torch's current HIP
+stream and pass raw device pointers; every arithmetic step runs in the HIP
+kernels.  There is no fallback: if the library has not been built, calls
+raise.
+
+    lora_apply(y, x, A_stack, B_stack, seg_indptr, adapter_ids, scale)
+        y[i] += scale * (x[i] @ A_stack[a]) @ B_stack[a]   for row i of a segment naming a
+    sgmv_shrink(v, x, A_stack, seg_indptr, adapter_ids)
+        v[i] = x[i] @ A_stack[a]   (v float32)
+    sgmv_expand(y, v, B_stack, seg_indptr, adapter_ids, scale)
+        y[i] += scale * v[i] @ B_stack[a]
+
+The math is the LoRA correction y = xW + xAB computed per request as
+v_i = x_i A_i then v_i B_i over back-to-back stacked adapter matrices
+(Punica walkthrough, omica.com.cn/news/959180, sections 2.1-2.2).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_HERE, "libsgmv.so")
+
+SGMV_F32, SGMV_F16, SGMV_BF16 = 0, 1, 2
+SGMV_MAX_RANK = 128
+STATUS = {
+    0: "SGMV_OK", 1: "SGMV_ERR_NULL_PTR", 2: "SGMV_ERR_BAD_SHAPE", 3: "SGMV_ERR_BAD_DTYPE",
+    4: "SGMV_ERR_UNSUPPORTED", 5: "SGMV_ERR_WORKSPACE", 6: "SGMV_ERR_HIP",
+    7: "SGMV_ERR_BAD_SEGMENTS",
+}
+# (name, restype, argtypes) of every symbol the header declares.
+_i32, _sz, _vp, _f32 = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+ABI = [
+    ("sgmv_abi_version", ctypes.c_int, []),
+    ("sgmv_status_string", ctypes.c_char_p, [ctypes.c_int]),
+    ("sgmv_shrink_workspace_bytes", _sz, [_i32, _i32, _i32, _i32, _i32]),
+    ("sgmv_shrink", ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                   _vp, _sz, _vp]),
+    ("sgmv_expand", ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32,
+                                   _i32, _vp]),
+    ("lora_apply_workspace_bytes", _sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    ("lora_apply", ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                  _i32, _f32, _i32, _vp, _sz, _vp]),
+    ("sgmv_validate_segments", ctypes.c_int, [_vp, _vp, _i32, _i32, _i32]),
+]
+
+
+class SGMVError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {STATUS.get(code, code)}")
+        self.code = code
+
+
+_lib_handle = None
+_lib_lock = threading.Lock()
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded ``libsgmv.so`` with argument types set (raises if not built)."""
+    global _lib_handle
+    with _lib_lock:
+        if _lib_handle is None:
+            if not os.path.exists(LIBRARY):
+                raise RuntimeError(
+                    f"{LIBRARY} is missing: build it with "
+                    "`python -m segmented_gather_gemv_sgmv_amd.build` (there is no fallback)")
+            handle = ctypes.CDLL(LIBRARY)
+            for name, restype, argtypes in ABI:
+                fn = getattr(handle, name)
+                fn.restype = restype
+                fn.argtypes = argtypes
+            _lib_handle = handle
+    return _lib_handle
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise SGMVError(code, what)
+
+
+# -- torch marshalling -----------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(dtype) -> int:
+    torch = _torch()
+    codes = {torch.float32: SGMV_F32, torch.float16: SGMV_F16, torch.bfloat16: SGMV_BF16}
+    if dtype not in codes:
+        raise TypeError(f"unsupported dtype {dtype}; expected float32, float16 or bfloat16")
+    return codes[dtype]
+
+
+def _stream_ptr(device) -> int:
+    return _torch().cuda.current_stream(device).cuda_stream
+
+
+def _need(t, name, device, dtype=None, ndim=None):
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got {t.dim()}")
+
+
+def _segments(seg_indptr, adapter_ids, device):
+    torch = _torch()
+    _need(seg_indptr, "seg_indptr", device, torch.int32, 1)
+    _need(adapter_ids, "adapter_ids", device, torch.int32, 1)
+    if seg_indptr.numel() != adapter_ids.numel() + 1:
+        raise ValueError("seg_indptr must have exactly one more entry than adapter_ids")
+    return adapter_ids.numel()
+
+
+class _WorkspaceCache:
+    """One growable device buffer per (device, stream); calls on one stream
+    run in order, so reusing its buffer between them is safe."""
+
+    def __init__(self):
+        self._bufs = {}
+        self._lock = threading.Lock()
+
+    def get(self, device, stream: int, nbytes: int):
+        torch = _torch()
+        key = (device, stream)
+        with self._lock:
+            buf = self._bufs.get(key)
+            if buf is None or buf.numel() < nbytes:
+                buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+                self._bufs[key] = buf
+            return buf
+
+
+_workspaces = _WorkspaceCache()
+
+
+def shrink_workspace_bytes(num_rows, num_segments, H1, r, dtype) -> int:
+    return int(lib().sgmv_shrink_workspace_bytes(num_rows, num_segments, H1, r, dtype_code(dtype)))
+
+
+def lora_apply_workspace_bytes(num_rows, num_segments, H1, H2, r, dtype) -> int:
+    return int(lib().lora_apply_workspace_bytes(num_rows, num_segments, H1, H2, r,
+                                                dtype_code(dtype)))
+
+
+def sgmv_shrink(v, x, A_stack, seg_indptr, adapter_ids, workspace=None):
+    """v[i, :] = x[i, :] @ A_stack[a] (float32 v, overwritten for covered rows)."""
+    torch = _torch()
+    dev = x.device
+    _need(x, "x", dev, None, 2)
+    _need(A_stack, "A_stack", dev, x.dtype, 3)
+    _need(v, "v", dev, torch.float32, 2)
+    S = _segments(seg_indptr, adapter_ids, dev)
+    R, H1 = x.shape
+    N, H1a, r = A_stack.shape
+    if H1a != H1 or tuple(v.shape) != (R, r):
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)}, A_stack {tuple(A_stack.shape)}, "
+                         f"v {tuple(v.shape)}")
+    dt = dtype_code(x.dtype)
+    stream = _stream_ptr(dev)
+    need = shrink_workspace_bytes(R, S, H1, r, x.dtype)
+    if workspace is None and need > 0:
+        workspace = _workspaces.get(dev, stream, need)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().sgmv_shrink(v.data_ptr(), x.data_ptr(), A_stack.data_ptr(), seg_indptr.data_ptr(),
+                             adapter_ids.data_ptr(), S, R, N, H1, r, dt, ws_ptr, ws_bytes, stream),
+           "sgmv_shrink")
+    return v
+
+
+def sgmv_expand(y, v, B_stack, seg_indptr, adapter_ids, scale=1.0):
+    """y[i, :] += scale * v[i, :] @ B_stack[a], rounded once to y's dtype."""
+    torch = _torch()
+    dev = y.device
+    _need(y, "y", dev, None, 2)
+    _need(B_stack, "B_stack", dev, y.dtype, 3)
+    _need(v, "v", dev, torch.float32, 2)
+    S = _segments(seg_indptr, adapter_ids, dev)
+    R, H2 = y.shape
+    N, r, H2b = B_stack.shape
+    if H2b != H2 or tuple(v.shape) != (R, r):
+        raise ValueError(f"shape mismatch: y {tuple(y.shape)}, B_stack {tuple(B_stack.shape)}, "
+                         f"v {tuple(v.shape)}")
+    _check(lib().sgmv_expand(y.data_ptr(), v.data_ptr(), B_stack.data_ptr(), seg_indptr.data_ptr(),
+                             adapter_ids.data_ptr(), S, R, N, r, H2, float(scale),
+                             dtype_code(y.dtype), _stream_ptr(dev)),
+           "sgmv_expand")
+    return y
+
+
+def lora_apply(y, x, A_stack, B_stack, seg_indptr, adapter_ids, scale=1.0, workspace=None):
+    """y[i, :] += scale * (x[i, :] @ A_stack[a]) @ B_stack[a], fp32 accumulation."""
+    dev = x.device
+    _need(x, "x", dev, None, 2)
+    _need(y, "y", dev, x.dtype, 2)
+    _need(A_stack, "A_stack", dev, x.dtype, 3)
+    _need(B_stack, "B_stack", dev, x.dtype, 3)
+    S = _segments(seg_indptr, adapter_ids, dev)
+    R, H1 = x.shape
+    N, H1a, r = A_stack.shape
+    Nb, rb, H2 = B_stack.shape
+    if H1a != H1 or Nb != N or rb != r or tuple(y.shape) != (R, H2):
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)}, y {tuple(y.shape)}, "
+                         f"A_stack {tuple(A_stack.shape)}, B_stack {tuple(B_stack.shape)}")
+    dt = dtype_code(x.dtype)
+    stream = _stream_ptr(dev)
+    need = lora_apply_workspace_bytes(R, S, H1, H2, r, x.dtype)
+    if workspace is None:
+        workspace = _workspaces.get(dev, stream, need)
+    _check(lib().lora_apply(y.data_ptr(), x.data_ptr(), A_stack.data_ptr(), B_stack.data_ptr(),
+                            seg_indptr.data_ptr(), adapter_ids.data_ptr(), S, R, N, H1, H2, r,
+                            float(scale), dt, workspace.data_ptr(),
+                            workspace.numel() * workspace.element_size(), stream),
+           "lora_apply")
+    return y
+
+
+def validate_segments(seg_indptr, adapter_ids, num_rows, num_adapters) -> int:
+    """Check a host (CPU) copy of a segment table; returns the status code."""
+    import numpy as np
+    seg = np.ascontiguousarray(np.asarray(seg_indptr), dtype=np.int32)
+    ids = np.ascontiguousarray(np.asarray(adapter_ids), dtype=np.int32)
+    if seg.ndim != 1 or ids.ndim != 1 or seg.shape[0] != ids.shape[0] + 1:
+        raise ValueError("seg_indptr must have exactly one more entry than adapter_ids")
+    return int(lib().sgmv_validate_segments(seg.ctypes.data, ids.ctypes.data if ids.size else None,
+                                            ids.shape[0], num_rows, num_adapters))
+
+
+__all__ = [
+    "lora_apply", "sgmv_shrink", "sgmv_expand", "lora_apply_workspace_bytes",
+    "shrink_workspace_bytes", "validate_segments", "lib", "SGMVError", "ABI", "LIBRARY",
+]

@@ -1,0 +1,356 @@
+// sgmv_api.hip -- the C ABI of libsgmv.so (declared in include/sgmv.h):
+// argument checks, the launch plan (grid sizes and the split of the H1
+// reduction, a pure function of the shapes so the workspace size can be
+// queried ahead of time), and kernel dispatch on element type and rank.
+//
+// No call allocates memory, keeps state or synchronises the host: kernels
+// are enqueued on the caller's stream and the call returns.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "sgmv.h"
+#include "sgmv_device.hpp"
+#include "sgmv_gemv.hpp"
+
+namespace {
+
+using namespace sgmv;
+
+constexpr int kShrinkThreads = 256;  // threads per shrink workgroup
+constexpr int kShrinkRows = 8;       // rows per shrink tile
+constexpr int kShrinkPG = 4;         // A loads in flight per lane
+constexpr int kExpandRows = 4;       // rows per expand tile
+constexpr int kGenericRows = 4;      // rows per tile in the general kernels
+constexpr int kGenericThreads = 256;
+constexpr int kTargetWorkgroups = 1024;  // at least four per CU on 256 CUs
+constexpr long long kMinChunkBytes = 4096;  // smallest A chunk worth a workgroup
+constexpr long long kMaxGrid = 0x7FFFFFFFLL;
+
+int elem_bytes(int dtype) { return dtype == SGMV_F32 ? 4 : 2; }
+int vec_width(int dtype) { return dtype == SGMV_F32 ? 4 : 8; }
+
+// Ranks with a vectorised kernel: r a multiple of the vector width with
+// r / VEC dividing the wave.
+bool vec_rank(int dtype, int r) {
+    switch (r) {
+        case 4: return dtype == SGMV_F32;
+        case 8: case 16: case 32: case 64: case 128: return true;
+        default: return false;
+    }
+}
+
+// Tile slots of a launch whose kernel cuts segments into tiles of `rows`
+// rows (see locate_tile): an upper bound on the number of tiles.
+long long tile_slots(int num_segments, int num_rows, int rows) {
+    return (long long)num_segments + num_rows / rows;
+}
+
+struct Plan {
+    int ksplit;       // chunks of the H1 reduction
+    int h_per_split;  // rows of A per chunk
+    int num_segments, num_rows;
+};
+
+// Pure function of the shapes (not of pointers), so that the workspace size
+// reported before a call matches what the call uses.
+Plan make_plan(int num_rows, int num_segments, int H1, int r, int dtype) {
+    Plan p;
+    p.num_segments = num_segments;
+    p.num_rows = num_rows;
+    const bool vec = vec_rank(dtype, r);
+    // The split is sized with the vectorised kernel's tile height whichever
+    // kernel runs, so that it stays a function of the shapes alone.
+    const long long slots = tile_slots(num_segments, num_rows, vec ? kShrinkRows : kGenericRows);
+
+    // Enough workgroups to fill the chip, but no chunk below kMinChunkBytes.
+    const long long a_bytes = (long long)H1 * r * elem_bytes(dtype);
+    long long maxk = a_bytes / kMinChunkBytes;
+    if (maxk < 1) maxk = 1;
+    long long want = (kTargetWorkgroups + slots - 1) / (slots > 0 ? slots : 1);
+    long long k = 1;
+    while (k < want && k * 2 <= maxk) k *= 2;
+    // Chunk boundaries on whole block-wide passes of the vectorised kernel.
+    const int unit = vec ? kShrinkThreads / (r / vec_width(dtype)) : 64;
+    long long hps = (H1 + k - 1) / k;
+    hps = (hps + unit - 1) / unit * unit;
+    p.h_per_split = (int)hps;
+    p.ksplit = (int)((H1 + hps - 1) / hps);
+    return p;
+}
+
+size_t partial_bytes(const Plan& p, int num_rows, int r) {
+    return (size_t)p.ksplit * (size_t)num_rows * (size_t)r * sizeof(float);
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_common(int num_segments, int num_rows, int num_adapters, int r, int dtype) {
+    if (dtype != SGMV_F32 && dtype != SGMV_F16 && dtype != SGMV_BF16) return SGMV_ERR_BAD_DTYPE;
+    if (num_segments < 0 || num_rows < 0 || num_adapters < 0) return SGMV_ERR_BAD_SHAPE;
+    if (r < 1 || r > SGMV_MAX_RANK) return SGMV_ERR_BAD_SHAPE;
+    return SGMV_OK;
+}
+
+int launch_status() {
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? SGMV_OK : SGMV_ERR_HIP;
+}
+
+// -- shrink dispatch ---------------------------------------------------------
+template <typename DT, int R>
+void launch_shrink_vec(float* out, long long out_stride, const void* x, const void* A,
+                       const int32_t* seg, const int32_t* ids, int S, int rows, int nad, int H1,
+                       const Plan& p, hipStream_t st) {
+    using T = typename DT::storage;
+    const unsigned grid = (unsigned)(tile_slots(S, rows, kShrinkRows) * p.ksplit);
+    hipLaunchKernelGGL((shrink_vec_kernel<DT, R, kShrinkThreads, kShrinkRows, kShrinkPG>),
+                       dim3(grid), dim3(kShrinkThreads), 0, st, out, out_stride,
+                       (const T*)x, (const T*)A, seg, ids, S, rows, nad, H1, p.ksplit,
+                       p.h_per_split);
+}
+
+template <typename DT>
+void launch_shrink_generic(float* out, long long out_stride, const void* x, const void* A,
+                           const int32_t* seg, const int32_t* ids, int S, int rows, int nad,
+                           int H1, int r, const Plan& p, hipStream_t st) {
+    using T = typename DT::storage;
+    const unsigned grid = (unsigned)(tile_slots(S, rows, kGenericRows) * p.ksplit);
+    hipLaunchKernelGGL((shrink_generic_kernel<DT, kGenericThreads, kGenericRows>), dim3(grid),
+                       dim3(kGenericThreads), 0, st, out, out_stride, (const T*)x, (const T*)A,
+                       seg, ids, S, rows, nad, H1, r, p.ksplit, p.h_per_split);
+}
+
+template <typename DT>
+void dispatch_shrink(float* out, long long out_stride, const void* x, const void* A,
+                     const int32_t* seg, const int32_t* ids, int S, int rows, int nad, int H1,
+                     int r, const Plan& p, hipStream_t st) {
+    const bool vec = vec_rank(std::is_same<DT, F32>::value ? SGMV_F32 : SGMV_F16, r) &&
+                     aligned16(A);
+    if (vec) {
+        switch (r) {
+            case 4:
+                if constexpr (DT::kVec == 4) {
+                    launch_shrink_vec<DT, 4>(out, out_stride, x, A, seg, ids, S, rows, nad, H1, p, st);
+                    return;
+                }
+                break;
+            case 8: launch_shrink_vec<DT, 8>(out, out_stride, x, A, seg, ids, S, rows, nad, H1, p, st); return;
+            case 16: launch_shrink_vec<DT, 16>(out, out_stride, x, A, seg, ids, S, rows, nad, H1, p, st); return;
+            case 32: launch_shrink_vec<DT, 32>(out, out_stride, x, A, seg, ids, S, rows, nad, H1, p, st); return;
+            case 64: launch_shrink_vec<DT, 64>(out, out_stride, x, A, seg, ids, S, rows, nad, H1, p, st); return;
+            case 128: launch_shrink_vec<DT, 128>(out, out_stride, x, A, seg, ids, S, rows, nad, H1, p, st); return;
+            default: break;
+        }
+    }
+    launch_shrink_generic<DT>(out, out_stride, x, A, seg, ids, S, rows, nad, H1, r, p, st);
+}
+
+// -- expand dispatch ---------------------------------------------------------
+template <typename DT, int R>
+void launch_expand_vec(void* y, const float* vpart, long long v_stride, int P, const void* B,
+                       const int32_t* seg, const int32_t* ids, int S, int rows, int nad, int H2,
+                       float scale, const Plan& p, hipStream_t st) {
+    using T = typename DT::storage;
+    constexpr int KB = R < 16 ? R : 16;
+    const int cw = kWave * DT::kVec;
+    const int csplit = (H2 + cw - 1) / cw;
+    const unsigned grid = (unsigned)(tile_slots(S, rows, kExpandRows) * csplit);
+    hipLaunchKernelGGL((expand_vec_kernel<DT, R, kExpandRows, KB>), dim3(grid), dim3(kWave), 0,
+                       st, (T*)y, vpart, v_stride, P, (const T*)B, seg, ids, S, rows, nad, H2,
+                       scale, csplit);
+}
+
+template <typename DT>
+void launch_expand_generic(void* y, const float* vpart, long long v_stride, int P, const void* B,
+                           const int32_t* seg, const int32_t* ids, int S, int rows, int nad,
+                           int r, int H2, float scale, const Plan& p, hipStream_t st) {
+    using T = typename DT::storage;
+    const int csplit = (H2 + kGenericThreads - 1) / kGenericThreads;
+    const unsigned grid = (unsigned)(tile_slots(S, rows, kGenericRows) * csplit);
+    hipLaunchKernelGGL((expand_generic_kernel<DT, kGenericThreads, kGenericRows>), dim3(grid),
+                       dim3(kGenericThreads), 0, st, (T*)y, vpart, v_stride, P, (const T*)B, seg,
+                       ids, S, rows, nad, r, H2, scale, csplit);
+}
+
+template <typename DT>
+void dispatch_expand(void* y, const float* vpart, long long v_stride, int P, const void* B,
+                     const int32_t* seg, const int32_t* ids, int S, int rows, int nad, int r,
+                     int H2, float scale, const Plan& p, hipStream_t st) {
+    const bool vec = vec_rank(std::is_same<DT, F32>::value ? SGMV_F32 : SGMV_F16, r) &&
+                     aligned16(B) && aligned16(y) && (H2 % DT::kVec == 0);
+    if (vec) {
+        switch (r) {
+            case 4:
+                if constexpr (DT::kVec == 4) {
+                    launch_expand_vec<DT, 4>(y, vpart, v_stride, P, B, seg, ids, S, rows, nad, H2, scale, p, st);
+                    return;
+                }
+                break;
+            case 8: launch_expand_vec<DT, 8>(y, vpart, v_stride, P, B, seg, ids, S, rows, nad, H2, scale, p, st); return;
+            case 16: launch_expand_vec<DT, 16>(y, vpart, v_stride, P, B, seg, ids, S, rows, nad, H2, scale, p, st); return;
+            case 32: launch_expand_vec<DT, 32>(y, vpart, v_stride, P, B, seg, ids, S, rows, nad, H2, scale, p, st); return;
+            case 64: launch_expand_vec<DT, 64>(y, vpart, v_stride, P, B, seg, ids, S, rows, nad, H2, scale, p, st); return;
+            case 128: launch_expand_vec<DT, 128>(y, vpart, v_stride, P, B, seg, ids, S, rows, nad, H2, scale, p, st); return;
+            default: break;
+        }
+    }
+    launch_expand_generic<DT>(y, vpart, v_stride, P, B, seg, ids, S, rows, nad, r, H2, scale, p, st);
+}
+
+template <typename F>
+void with_dtype(int dtype, F&& f) {
+    switch (dtype) {
+        case SGMV_F32: f(F32{}); break;
+        case SGMV_F16: f(F16{}); break;
+        default: f(BF16{}); break;
+    }
+}
+
+// The expand launch needs the row capacity of the partial buffer to fit the
+// grid; both launches index at most num_rows rows.
+// Whichever kernel a call ends up on, its grid must fit one launch.  The
+// general kernels have the shortest tiles and so the most slots.
+bool grid_fits(const Plan& p, int H2) {
+    const long long slots = tile_slots(p.num_segments, p.num_rows, kGenericRows);
+    const long long csplit = (H2 + kGenericThreads - 1) / kGenericThreads;
+    const long long csplit_vec = (H2 + kWave * 4 - 1) / (kWave * 4);
+    return slots * p.ksplit <= kMaxGrid && slots * csplit <= kMaxGrid &&
+           slots * csplit_vec <= kMaxGrid;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sgmv_abi_version(void) { return SGMV_ABI_VERSION; }
+
+const char* sgmv_status_string(int status) {
+    switch (status) {
+        case SGMV_OK: return "ok";
+        case SGMV_ERR_NULL_PTR: return "a required pointer is NULL";
+        case SGMV_ERR_BAD_SHAPE: return "invalid size or rank";
+        case SGMV_ERR_BAD_DTYPE: return "unknown dtype";
+        case SGMV_ERR_UNSUPPORTED: return "sizes exceed what the kernels index";
+        case SGMV_ERR_WORKSPACE: return "workspace missing or too small";
+        case SGMV_ERR_HIP: return "HIP launch error";
+        case SGMV_ERR_BAD_SEGMENTS: return "malformed segment table";
+        default: return "unknown status";
+    }
+}
+
+size_t sgmv_shrink_workspace_bytes(int32_t num_rows, int32_t num_segments, int32_t H1, int32_t r,
+                                   int32_t dtype) {
+    if (check_common(num_segments, num_rows, 0, r, dtype) != SGMV_OK || H1 < 1) return 0;
+    const Plan p = make_plan(num_rows, num_segments, H1, r, dtype);
+    return p.ksplit > 1 ? partial_bytes(p, num_rows, r) : 0;
+}
+
+size_t lora_apply_workspace_bytes(int32_t num_rows, int32_t num_segments, int32_t H1, int32_t H2,
+                                  int32_t r, int32_t dtype) {
+    if (check_common(num_segments, num_rows, 0, r, dtype) != SGMV_OK || H1 < 1 || H2 < 1) return 0;
+    const Plan p = make_plan(num_rows, num_segments, H1, r, dtype);
+    return partial_bytes(p, num_rows, r);
+}
+
+int sgmv_shrink(float* v, const void* x, const void* A_stack, const int32_t* seg_indptr,
+                const int32_t* adapter_ids, int32_t num_segments, int32_t num_rows,
+                int32_t num_adapters, int32_t H1, int32_t r, int32_t dtype, void* workspace,
+                size_t workspace_bytes, void* stream) {
+    int rc = check_common(num_segments, num_rows, num_adapters, r, dtype);
+    if (rc != SGMV_OK) return rc;
+    if (H1 < 1) return SGMV_ERR_BAD_SHAPE;
+    if (num_rows == 0 || num_segments == 0) return SGMV_OK;
+    if (!v || !x || !A_stack || !seg_indptr || !adapter_ids) return SGMV_ERR_NULL_PTR;
+    const Plan p = make_plan(num_rows, num_segments, H1, r, dtype);
+    if (!grid_fits(p, 1)) return SGMV_ERR_UNSUPPORTED;
+    const size_t need = p.ksplit > 1 ? partial_bytes(p, num_rows, r) : 0;
+    if (need > 0 && (!workspace || workspace_bytes < need)) return SGMV_ERR_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    float* out = p.ksplit > 1 ? (float*)workspace : v;
+    const long long stride = (long long)num_rows * r;
+    with_dtype(dtype, [&](auto dt) {
+        using DT = decltype(dt);
+        dispatch_shrink<DT>(out, stride, x, A_stack, seg_indptr, adapter_ids, num_segments,
+                            num_rows, num_adapters, H1, r, p, st);
+    });
+    if ((rc = launch_status()) != SGMV_OK) return rc;
+    if (p.ksplit > 1) {
+        const long long n = stride;
+        const unsigned grid = (unsigned)((n + 255) / 256);
+        hipLaunchKernelGGL(reduce_partials_kernel, dim3(grid), dim3(256), 0, st, v, out, stride,
+                           p.ksplit, seg_indptr, adapter_ids, num_segments, num_rows,
+                           num_adapters, r);
+        rc = launch_status();
+    }
+    return rc;
+}
+
+int sgmv_expand(void* y, const float* v, const void* B_stack, const int32_t* seg_indptr,
+                const int32_t* adapter_ids, int32_t num_segments, int32_t num_rows,
+                int32_t num_adapters, int32_t r, int32_t H2, float scale, int32_t dtype,
+                void* stream) {
+    int rc = check_common(num_segments, num_rows, num_adapters, r, dtype);
+    if (rc != SGMV_OK) return rc;
+    if (H2 < 1) return SGMV_ERR_BAD_SHAPE;
+    if (num_rows == 0 || num_segments == 0) return SGMV_OK;
+    if (!y || !v || !B_stack || !seg_indptr || !adapter_ids) return SGMV_ERR_NULL_PTR;
+    const Plan p = make_plan(num_rows, num_segments, 1, r, dtype);
+    if (!grid_fits(p, H2)) return SGMV_ERR_UNSUPPORTED;
+    hipStream_t st = (hipStream_t)stream;
+    with_dtype(dtype, [&](auto dt) {
+        using DT = decltype(dt);
+        dispatch_expand<DT>(y, v, 0, 1, B_stack, seg_indptr, adapter_ids, num_segments, num_rows,
+                            num_adapters, r, H2, scale, p, st);
+    });
+    return launch_status();
+}
+
+int lora_apply(void* y, const void* x, const void* A_stack, const void* B_stack,
+               const int32_t* seg_indptr, const int32_t* adapter_ids, int32_t num_segments,
+               int32_t num_rows, int32_t num_adapters, int32_t H1, int32_t H2, int32_t r,
+               float scale, int32_t dtype, void* workspace, size_t workspace_bytes,
+               void* stream) {
+    int rc = check_common(num_segments, num_rows, num_adapters, r, dtype);
+    if (rc != SGMV_OK) return rc;
+    if (H1 < 1 || H2 < 1) return SGMV_ERR_BAD_SHAPE;
+    if (num_rows == 0 || num_segments == 0) return SGMV_OK;
+    if (!y || !x || !A_stack || !B_stack || !seg_indptr || !adapter_ids) return SGMV_ERR_NULL_PTR;
+    const Plan p = make_plan(num_rows, num_segments, H1, r, dtype);
+    if (!grid_fits(p, H2)) return SGMV_ERR_UNSUPPORTED;
+    const size_t need = partial_bytes(p, num_rows, r);
+    if (!workspace || workspace_bytes < need) return SGMV_ERR_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    float* part = (float*)workspace;
+    const long long stride = (long long)num_rows * r;
+    with_dtype(dtype, [&](auto dt) {
+        using DT = decltype(dt);
+        dispatch_shrink<DT>(part, stride, x, A_stack, seg_indptr, adapter_ids, num_segments,
+                            num_rows, num_adapters, H1, r, p, st);
+    });
+    if ((rc = launch_status()) != SGMV_OK) return rc;
+    with_dtype(dtype, [&](auto dt) {
+        using DT = decltype(dt);
+        dispatch_expand<DT>(y, part, stride, p.ksplit, B_stack, seg_indptr, adapter_ids,
+                            num_segments, num_rows, num_adapters, r, H2, scale, p, st);
+    });
+    return launch_status();
+}
+
+int sgmv_validate_segments(const int32_t* h_seg_indptr, const int32_t* h_adapter_ids,
+                           int32_t num_segments, int32_t num_rows, int32_t num_adapters) {
+    if (num_segments < 0 || num_rows < 0 || num_adapters < 0) return SGMV_ERR_BAD_SHAPE;
+    if (!h_seg_indptr) return SGMV_ERR_NULL_PTR;
+    if (num_segments > 0 && !h_adapter_ids) return SGMV_ERR_NULL_PTR;
+    if (h_seg_indptr[0] < 0) return SGMV_ERR_BAD_SEGMENTS;
+    for (int32_t s = 0; s < num_segments; ++s) {
+        if (h_seg_indptr[s + 1] < h_seg_indptr[s]) return SGMV_ERR_BAD_SEGMENTS;
+        if (h_adapter_ids[s] < 0 || h_adapter_ids[s] >= num_adapters) return SGMV_ERR_BAD_SEGMENTS;
+    }
+    if (h_seg_indptr[num_segments] > num_rows) return SGMV_ERR_BAD_SEGMENTS;
+    return SGMV_OK;
+}
+
+}  // extern "C"

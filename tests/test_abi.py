@@ -1,0 +1,132 @@
+"""CPU checks of the C ABI boundary: the library loads, exports every symbol
+the header declares, and rejects bad arguments before enqueueing anything.
+No call here launches a kernel (there is no GPU on this side)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import segmented_gather_gemv_sgmv_amd as sg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sgmv.h")
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sg.LIBRARY):
+        from segmented_gather_gemv_sgmv_amd import build
+        build.build()
+    return sg.lib()
+
+
+def test_header_symbols_exported(lib):
+    names = _header_functions()
+    assert {"lora_apply", "sgmv_shrink", "sgmv_expand"} <= names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in sgmv.h but not exported"
+    assert names == {n for n, _, _ in sg.ABI}, "binding table and header disagree"
+
+
+def test_abi_version_matches_header(lib):
+    m = re.search(r"#define\s+SGMV_ABI_VERSION\s+(\d+)", open(HEADER).read())
+    assert lib.sgmv_abi_version() == int(m.group(1))
+
+
+def test_status_strings(lib):
+    for code in range(0, 8):
+        s = lib.sgmv_status_string(code)
+        assert isinstance(s, bytes) and len(s) > 0
+    assert lib.sgmv_status_string(0) == b"ok"
+    assert lib.sgmv_status_string(99) == b"unknown status"
+
+
+FAKE = 0x1000  # a non-null, 16-byte-aligned value; never dereferenced on these paths
+
+
+def _apply(lib, **kw):
+    a = dict(y=FAKE, x=FAKE, A=FAKE, B=FAKE, seg=FAKE, ids=FAKE, S=4, R=16, N=4, H1=256, H2=256,
+             r=8, scale=1.0, dtype=0, ws=FAKE, ws_bytes=0, stream=None)
+    a.update(kw)
+    return lib.lora_apply(a["y"], a["x"], a["A"], a["B"], a["seg"], a["ids"], a["S"], a["R"],
+                          a["N"], a["H1"], a["H2"], a["r"], a["scale"], a["dtype"], a["ws"],
+                          a["ws_bytes"], a["stream"])
+
+
+def test_lora_apply_rejects_bad_arguments(lib):
+    assert _apply(lib, dtype=7) == 3
+    assert _apply(lib, r=0) == 2
+    assert _apply(lib, r=129) == 2
+    assert _apply(lib, H1=0) == 2
+    assert _apply(lib, H2=-1) == 2
+    assert _apply(lib, R=-1) == 2
+    assert _apply(lib, S=-2) == 2
+    assert _apply(lib, N=-1) == 2
+    for p in ("y", "x", "A", "B", "seg", "ids"):
+        assert _apply(lib, **{p: None}) == 1, p
+    need = lib.lora_apply_workspace_bytes(16, 4, 256, 256, 8, 0)
+    assert need > 0
+    assert _apply(lib, ws=None, ws_bytes=need) == 5
+    assert _apply(lib, ws_bytes=need - 1) == 5
+
+
+def test_empty_batches_are_noops(lib):
+    # nothing is enqueued, so NULL pointers are fine
+    none = dict(y=None, x=None, A=None, B=None, seg=None, ids=None, ws=None)
+    assert _apply(lib, R=0, **none) == 0
+    assert _apply(lib, S=0, **none) == 0
+    assert lib.sgmv_shrink(None, None, None, None, None, 0, 5, 1, 64, 8, 1, None, 0, None) == 0
+    assert lib.sgmv_expand(None, None, None, None, None, 3, 0, 1, 8, 64, 1.0, 1, None) == 0
+
+
+def test_shrink_expand_reject_bad_arguments(lib):
+    assert lib.sgmv_shrink(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 16, 4, 256, 8, 5, None, 0, None) == 3
+    assert lib.sgmv_shrink(FAKE, None, FAKE, FAKE, FAKE, 4, 16, 4, 256, 8, 1, None, 0, None) == 1
+    assert lib.sgmv_shrink(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 16, 4, 0, 8, 1, None, 0, None) == 2
+    need = lib.sgmv_shrink_workspace_bytes(64, 64, 4096, 16, 1)
+    assert need > 0  # the H1 reduction is split for this shape
+    assert lib.sgmv_shrink(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 64, 4096, 16, 1, None, need,
+                           None) == 5
+    assert lib.sgmv_expand(FAKE, FAKE, None, FAKE, FAKE, 4, 16, 4, 8, 256, 1.0, 1, None) == 1
+    assert lib.sgmv_expand(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 16, 4, 200, 256, 1.0, 1, None) == 2
+
+
+def test_workspace_sizes(lib):
+    for R, S, H1, H2, r, dt in [(64, 64, 4096, 4096, 16, 1), (4096, 16, 4096, 4096, 16, 1),
+                                (256, 110, 5120, 13824, 64, 2), (16, 4, 256, 256, 8, 0),
+                                (7, 3, 100, 90, 5, 1)]:
+        n = lib.lora_apply_workspace_bytes(R, S, H1, H2, r, dt)
+        assert n >= R * r * 4 and n % (R * r * 4) == 0
+        assert n == lib.lora_apply_workspace_bytes(R, S, H1, H2, r, dt)
+        m = lib.sgmv_shrink_workspace_bytes(R, S, H1, r, dt)
+        assert m in (0, n)
+    assert lib.lora_apply_workspace_bytes(16, 4, 256, 256, 0, 0) == 0
+
+
+def test_validate_segments():
+    ok = sg.validate_segments([0, 2, 2, 5], [1, 0, 3], num_rows=6, num_adapters=4)
+    assert ok == 0
+    assert sg.validate_segments([0], [], num_rows=0, num_adapters=0) == 0
+    assert sg.validate_segments([0, 3, 2], [0, 0], 6, 4) == 7       # decreasing
+    assert sg.validate_segments([0, 3, 7], [0, 0], 6, 4) == 7       # past num_rows
+    assert sg.validate_segments([-1, 3], [0], 6, 4) == 7            # negative start
+    assert sg.validate_segments([0, 3], [4], 6, 4) == 7             # id out of range
+    assert sg.validate_segments([0, 3], [-1], 6, 4) == 7
+    with pytest.raises(ValueError):
+        sg.validate_segments([0, 3], [0, 1], 6, 4)
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    import importlib
+    monkeypatch.setattr(sg, "LIBRARY", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(sg, "_lib_handle", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        sg.lib()

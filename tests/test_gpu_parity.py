@@ -1,0 +1,235 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle.
+
+Covers the five reference workloads at full size (every output element),
+random shapes that span several tiles and ragged tails for every dtype and a
+range of ranks (vectorised and general kernels), exact integer inputs that
+must match bit for bit, edge cases of the segment table, misaligned
+pointers, determinism and HIP graph replay.
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from gpu_helpers import (assert_close, gpu_expand, gpu_lora_apply, gpu_shrink, to_device,
+                         torch_dtype)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU (run with -m 'not gpu' on CPU)"
+    import segmented_gather_gemv_sgmv_amd as sg
+    sg.lib()  # fail loudly if the HIP library is missing
+    yield
+
+
+_cache = {}
+
+
+def _config(key):
+    if key not in _cache:
+        i, ctl = key
+        w = wl.config(i, control=ctl)
+        y, v = oracle.lora_apply(w.y0, w.x, w.A, w.B, w.seg_indptr, w.adapter_ids, w.scale)
+        _cache.clear()  # keep at most one full-size workload in memory
+        _cache[key] = (w, y, v)
+    return _cache[key]
+
+
+CONFIG_KEYS = [(0, False), (1, False), (2, False), (2, True), (3, False), (4, False)]
+CONFIG_IDS = ["tiny", "llama7b_decode", "skewed_zipf", "skewed_control", "prefill", "mlp_up"]
+
+
+@pytest.mark.parametrize("key", CONFIG_KEYS, ids=CONFIG_IDS)
+def test_config_all_entry_points(key):
+    w, y_ref, v_ref = _config(key)
+    d = to_device(w)
+    assert_close(gpu_lora_apply(w, d), y_ref, w.dtype, f"lora_apply {w.name}")
+    assert_close(gpu_shrink(w, d), v_ref, w.dtype, f"sgmv_shrink {w.name}")
+    # expand alone, fed the oracle's v rounded to float32
+    y_e = oracle.expand(w.y0, v_ref.astype(np.float32), w.B, w.seg_indptr, w.adapter_ids, w.scale)
+    assert_close(gpu_expand(w, v_ref, d), y_e, w.dtype, f"sgmv_expand {w.name}")
+
+
+RANDOM_CASES = [
+    # dtype, H1, H2, r, adapters, rows, segments
+    ("f32", 256, 256, 8, 4, 16, 4),
+    ("f32", 1000, 776, 4, 7, 53, 9),
+    ("f32", 513, 300, 16, 5, 37, 6),
+    ("f32", 2048, 1024, 64, 3, 19, 3),
+    ("f32", 300, 260, 128, 2, 9, 2),
+    ("f16", 4096, 4096, 16, 9, 70, 11),
+    ("f16", 1536, 2560, 8, 6, 100, 5),
+    ("f16", 1000, 1000, 32, 4, 45, 7),
+    ("f16", 640, 1032, 64, 5, 33, 4),
+    ("f16", 520, 904, 128, 3, 21, 3),
+    ("bf16", 5120, 1384, 64, 8, 40, 12),
+    ("bf16", 2048, 2048, 16, 10, 77, 20),
+    ("bf16", 777, 999, 8, 4, 29, 5),
+    # general kernel: ranks without a vector kernel, ragged H2
+    ("f16", 300, 250, 1, 3, 17, 4),
+    ("f16", 513, 257, 3, 4, 23, 5),
+    ("bf16", 1024, 700, 12, 5, 31, 6),
+    ("f32", 400, 333, 5, 3, 14, 3),
+    ("f16", 256, 384, 4, 3, 12, 3),
+    ("bf16", 384, 128, 100, 2, 9, 2),
+]
+
+
+@pytest.mark.parametrize("case", RANDOM_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_random_shapes(case):
+    dtype, H1, H2, r, N, R, S = case
+    w = wl.small_random(zlib.crc32(repr(case).encode()), dtype, H1, H2, r, N, R, S, allow_empty=True,
+                        uncovered_tail=R // 7)
+    y_ref, v_ref = oracle.lora_apply(w.y0, w.x, w.A, w.B, w.seg_indptr, w.adapter_ids, w.scale)
+    d = to_device(w)
+    assert_close(gpu_lora_apply(w, d), y_ref, dtype, "lora_apply")
+    cov = int(w.seg_indptr[-1])
+    v = gpu_shrink(w, d, fill=-3.5)
+    assert_close(v[:cov], v_ref[:cov], dtype, "sgmv_shrink")
+    assert np.all(v[cov:] == -3.5), "shrink wrote rows outside every segment"
+
+
+@pytest.mark.parametrize("dtype,r", [("f32", 8), ("f32", 5), ("f16", 16), ("f16", 64),
+                                     ("f16", 3), ("bf16", 16), ("bf16", 64), ("bf16", 12)])
+def test_integer_inputs_match_bit_for_bit(dtype, r):
+    # {-1,0,1} inputs: every partial sum is a small integer, exact in float32
+    w = wl.integer_exact(11 + r, dtype, 1536, 1040, r, 6, 67, 9, density=0.08, scale=2.0)
+    y_ref, v_ref = oracle.lora_apply(w.y0, w.x, w.A, w.B, w.seg_indptr, w.adapter_ids, w.scale)
+    assert np.abs(y_ref).max() < 256  # exact in every output dtype
+    d = to_device(w)
+    assert np.array_equal(gpu_lora_apply(w, d), y_ref)
+    cov = int(w.seg_indptr[-1])
+    assert np.array_equal(gpu_shrink(w, d)[:cov], v_ref[:cov])
+
+
+def test_long_segments_and_many_segments():
+    # one long segment (many row tiles) plus > 256 short ones (multi-pass tile scan)
+    rng = np.random.default_rng(5)
+    lengths = [300] + list(rng.integers(0, 3, size=700)) + [41]
+    ids = rng.integers(0, 40, size=len(lengths))
+    w = wl.make_workload("long_and_many", "f16", 512, 768, 16, 40, lengths, ids, 1.25, seed=6)
+    y_ref, _ = oracle.lora_apply(w.y0, w.x, w.A, w.B, w.seg_indptr, w.adapter_ids, w.scale)
+    assert_close(gpu_lora_apply(w), y_ref, "f16", "long and many segments")
+
+
+def test_empty_and_degenerate_tables():
+    import torch
+    import segmented_gather_gemv_sgmv_amd as sg
+    w = wl.small_random(3, "f16", 256, 512, 16, 4, 20, 5)
+    d = to_device(w)
+    # no segments, and segments that are all empty: y unchanged
+    for seg, ids in [(np.array([0], np.int32), np.array([], np.int32)),
+                     (np.array([0, 0, 0, 0], np.int32), np.array([1, 2, 3], np.int32))]:
+        y = d["y0"].clone()
+        sg.lora_apply(y, d["x"], d["A"], d["B"], torch.from_numpy(seg).cuda(),
+                      torch.from_numpy(ids).cuda(), 2.0)
+        torch.cuda.synchronize()
+        assert torch.equal(y, d["y0"])
+    # zero rows
+    e = torch.empty((0, 256), dtype=torch.float16, device="cuda")
+    ey = torch.empty((0, 512), dtype=torch.float16, device="cuda")
+    sg.lora_apply(ey, e, d["A"], d["B"], torch.zeros(1, dtype=torch.int32, device="cuda"),
+                  torch.zeros(0, dtype=torch.int32, device="cuda"), 1.0)
+    # a segment starting at the last row, and a single-row batch
+    for seg, R in [([19, 20], 20), ([0, 1], 1)]:
+        ws = wl.make_workload("edge", "f16", 256, 512, 16, 4, [0] * 0 + [seg[1] - seg[0]], [2],
+                              0.5, seed=4, num_rows=R)
+        ws.seg_indptr = np.array(seg, np.int32)
+        y_ref, _ = oracle.lora_apply(ws.y0, ws.x, ws.A, ws.B, ws.seg_indptr, ws.adapter_ids,
+                                     ws.scale)
+        assert_close(gpu_lora_apply(ws), y_ref, "f16", f"edge {seg}")
+
+
+def test_zero_B_or_scale_leaves_y_bitwise():
+    w = wl.small_random(8, "bf16", 1024, 1024, 16, 5, 40, 6)
+    d = to_device(w)
+    d["B"].zero_()
+    assert np.array_equal(gpu_lora_apply(w, d), w.y0.astype(np.float64))
+    d = to_device(w)
+    w.scale = 0.0
+    assert np.array_equal(gpu_lora_apply(w, d), w.y0.astype(np.float64))
+
+
+def test_invalid_adapter_ids_are_skipped():
+    """Segments naming an adapter outside the stack are skipped by the kernels'
+    guards: their rows stay as they were, the other segments are computed."""
+    w = wl.small_random(9, "f16", 512, 512, 16, 4, 24, 4, allow_empty=False)
+    good = w.adapter_ids.copy()
+    bad = good.copy()
+    bad[1] = 4        # == num_adapters
+    bad[3] = -7
+    d = to_device(w)
+    import torch
+    d["ids"] = torch.from_numpy(bad).cuda()
+    y = gpu_lora_apply(w, d)
+    y_ref, _ = oracle.lora_apply(w.y0, w.x, w.A, w.B, w.seg_indptr, good, w.scale)
+    for s in range(4):
+        rows = slice(int(w.seg_indptr[s]), int(w.seg_indptr[s + 1]))
+        if s in (1, 3):
+            assert np.array_equal(y[rows], w.y0[rows].astype(np.float64))
+        else:
+            assert_close(y[rows], y_ref[rows], "f16", f"segment {s}")
+
+
+def test_misaligned_pointers_take_general_path():
+    import torch
+    import segmented_gather_gemv_sgmv_amd as sg
+    w = wl.small_random(10, "f16", 1024, 1024, 16, 4, 30, 5)
+    y_ref, _ = oracle.lora_apply(w.y0, w.x, w.A, w.B, w.seg_indptr, w.adapter_ids, w.scale)
+    d = to_device(w)
+
+    def shifted(t):  # same values, data pointer off by one element
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        view = buf[1:].view(t.shape)
+        view.copy_(t)
+        return view
+
+    y = shifted(d["y0"])
+    sg.lora_apply(y, shifted(d["x"]), shifted(d["A"]), shifted(d["B"]), d["seg"], d["ids"],
+                  w.scale)
+    torch.cuda.synchronize()
+    assert_close(y.double().cpu().numpy(), y_ref, "f16", "misaligned")
+
+
+def test_repeated_calls_are_bitwise_identical():
+    import torch
+    w = wl.config(1)
+    d = to_device(w)
+    outs = [gpu_lora_apply(w, d) for _ in range(3)]
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+def test_graph_replay_matches_eager():
+    """lora_apply captured in a HIP graph: every replay, with eager work and
+    synchronisations in between, equals the eager result."""
+    import torch
+    import segmented_gather_gemv_sgmv_amd as sg
+    w = wl.config(2)
+    d = to_device(w)
+    y_eager = torch.from_numpy(gpu_lora_apply(w, d))
+    ws = torch.empty(sg.lora_apply_workspace_bytes(w.num_rows, w.num_segments, w.H1, w.H2, w.r,
+                                                   torch_dtype(w.dtype)),
+                     dtype=torch.uint8, device="cuda")
+    y = d["y0"].clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        sg.lora_apply(y, d["x"], d["A"], d["B"], d["seg"], d["ids"], w.scale, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sg.lora_apply(y, d["x"], d["A"], d["B"], d["seg"], d["ids"], w.scale, workspace=ws)
+    for rep in range(4):
+        y.copy_(d["y0"])
+        junk = torch.randn(1 << 16, device="cuda").sum()  # unrelated eager work
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.double().cpu(), y_eager), f"replay {rep}"
+        del junk
