@@ -1,0 +1,218 @@
+#!/usr/bin/env python3
+"""Benchmark: SGMV LoRA add-on (lora_apply) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--report FILE]
+
+Workload: Llama-2-7B decode projection, H1 = H2 = 4096, r = 16, 64 rows in
+64 one-row segments (a distinct adapter per row), fp16 with fp32
+accumulation, scale 2.  One step = one lora_apply over the batch (segment
+lookup, shrink, expand, fused scale + accumulate into y).  Inputs are
+seeded synthetic arrays resident in HBM before timing starts.
+
+So that timed calls read HBM rather than the 256 MB Infinity Cache, the
+step rotates through enough copies of the inputs (same values, different
+addresses) to exceed 1 GiB.  The K timed steps are captured in one HIP graph
+(so host launch cost does not pace the GPU) and timed with HIP events on the
+stream they run on.
+
+Prints one JSON line: rows/s, ms per step, achieved algorithmic HBM GB/s
+and its fraction of the 8 TB/s peak (``roofline``), and the CPU oracle's
+rows/s on a bounded sample of the same workload (``cpu_baseline``).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0   # dense fp16/bf16, published
+MALL_BYTES = 256 << 20
+ROTATE_BYTES = 1 << 30          # >= 4x the Infinity Cache
+
+
+def algorithmic_bytes(w) -> int:
+    """What one call must move: each segment's A and B once, x once, y read
+    and written once (covered rows only)."""
+    e = w.elem_bytes
+    lens = w.seg_lengths
+    segs = int((lens > 0).sum())
+    rows = int(lens.sum())
+    weights = segs * (w.H1 * w.r + w.r * w.H2) * e
+    return weights + rows * w.H1 * e + 2 * rows * w.H2 * e
+
+
+def algorithmic_flops(w) -> int:
+    rows = int(w.seg_lengths.sum())
+    return 2 * rows * w.r * (w.H1 + w.H2)
+
+
+class BenchState:
+    """Device copies of a workload, rotated over `nsets` buffer sets."""
+
+    def __init__(self, w, nsets: int, device="cuda:0"):
+        import torch
+        import segmented_gather_gemv_sgmv_amd as sg
+        self.w = w
+        self.sg = sg
+        dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+        self.dtype = dt
+        dev = torch.device(device)
+        to = lambda a: torch.from_numpy(a).to(dev).to(dt)
+        base = dict(x=to(w.x), A=to(w.A), B=to(w.B), y0=to(w.y0))
+        self.seg = torch.from_numpy(w.seg_indptr).to(dev)
+        self.ids = torch.from_numpy(w.adapter_ids).to(dev)
+        self.sets = []
+        for i in range(nsets):
+            s = {k: (v if i == 0 else v.clone()) for k, v in base.items() if k != "y0"}
+            s["y"] = base["y0"].clone()
+            self.sets.append(s)
+        self.y0 = base["y0"]
+        nbytes = sg.lora_apply_workspace_bytes(w.num_rows, w.num_segments, w.H1, w.H2, w.r, dt)
+        self.workspace = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        self.device = dev
+
+    def step(self, i: int):
+        s = self.sets[i % len(self.sets)]
+        self.sg.lora_apply(s["y"], s["x"], s["A"], s["B"], self.seg, self.ids, self.w.scale,
+                           workspace=self.workspace)
+
+    def reset_outputs(self):
+        for s in self.sets:
+            s["y"].copy_(self.y0)
+
+    def capture(self, nsteps: int, first: int = 0):
+        """A HIP graph of `nsteps` consecutive steps starting at set `first`."""
+        import torch
+        side = torch.cuda.Stream(self.device)
+        side.wait_stream(torch.cuda.current_stream(self.device))
+        with torch.cuda.stream(side):
+            self.step(first)  # settle lazy initialisation off the capture
+        torch.cuda.current_stream(self.device).wait_stream(side)
+        torch.cuda.synchronize(self.device)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for k in range(nsteps):
+                self.step(first + k)
+        return g
+
+
+def run_gpu(w, steps: int, warmup: int, device="cuda:0"):
+    import torch
+    per_set = (w.x.size + w.A.size + w.B.size + w.y0.size) * w.elem_bytes
+    nsets = max(1, min(512, math.ceil(ROTATE_BYTES / max(per_set, 1))))
+    st = BenchState(w, nsets, device)
+    for i in range(warmup):
+        st.step(i)
+    torch.cuda.synchronize(device)
+    graph = st.capture(steps, first=warmup)
+    torch.cuda.synchronize(device)
+    stream = torch.cuda.current_stream(device)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    graph.replay()
+    end.record(stream)
+    torch.cuda.synchronize(device)
+    wall = time.perf_counter() - t0
+    gpu_ms = start.elapsed_time(end)
+    return dict(gpu_ms=gpu_ms, wall_s=wall, nsets=nsets, per_set_bytes=per_set)
+
+
+def cpu_baseline(w, budget_s: float = 10.0):
+    """The CPU oracle (single thread, plain fp64 loops) on the same batch."""
+    import oracle
+    orc = oracle.get()
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        orc.lora_apply(w.y0, w.x, w.A, w.B, w.seg_indptr, w.adapter_ids, w.scale)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    rows = int(w.seg_lengths.sum()) * calls
+    return dict(value=rows / el, unit="rows/s", cores=1, kind="oracle",
+                sample=f"{calls} full {w.num_rows}-row batches of the same workload "
+                       f"({el:.1f} s, one thread)")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--report", default=None, help="append per-workload JSON lines to FILE")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "SGMV shards by segments with no exchange, so per-GPU throughput is the "
+              "figure of interest.", file=sys.stderr)
+        return 2
+
+    import torch
+    import workloads as wl
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+
+    w = wl.llama7b_decode(seed=0)
+    res = run_gpu(w, args.steps, args.warmup)
+    step_s = res["gpu_ms"] / 1e3 / args.steps
+    rows = int(w.seg_lengths.sum())
+    abytes = algorithmic_bytes(w)
+    flops = algorithmic_flops(w)
+    achieved = abytes / step_s / 1e9
+    line = {
+        "metric": "SGMV rows/s and achieved HBM GB/s (% of peak) per layer call, H=4096 r=16",
+        "value": rows / step_s,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded; Llama-2-7B decode shapes, no weights)",
+        "config": {
+            "workload": w.name, "H1": w.H1, "H2": w.H2, "r": w.r, "rows": rows,
+            "segments": w.num_segments, "adapters_in_stack": w.num_adapters, "scale": w.scale,
+            "buffer_sets_rotated": res["nsets"], "launch": "hip graph of all timed steps",
+        },
+        "us_per_call": step_s * 1e6,
+        "achieved_hbm_GBps": achieved,
+        "hbm_peak_frac": achieved / HBM_PEAK_GBPS,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "lora_fused_kernel (one launch per step)",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": None,
+            "algorithmic_bytes_per_launch": abytes,
+            "tflops": flops / step_s / 1e12,
+        },
+        "wall_s_timed": res["wall_s"],
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

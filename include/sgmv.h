@@ -33,7 +33,8 @@
  * Pointers.  Every array argument is a DEVICE pointer owned by the caller
  * (the host-side validator is the one exception and says so).  The library
  * keeps no state between calls, allocates no memory and never synchronises
- * the host with the device: each call only enqueues kernels on `stream`
+ * the host with the device (sgmv_set_fused_wait() is the one process-wide
+ * setting): each call only enqueues kernels on `stream`
  * (a hipStream_t; NULL means the default stream) and returns.
  *
  * Segment table.  Rows outside every segment are left untouched; empty
@@ -43,6 +44,18 @@
  * kernels clamp segment bounds to [0, num_rows) and skip a segment whose
  * adapter id lies outside [0, num_adapters); what a malformed table computes
  * is otherwise unspecified.  sgmv_validate_segments() checks a host copy.
+ *
+ * Workspace.  sgmv_shrink and lora_apply take caller-owned device scratch
+ * (size from the *_workspace_bytes queries, a pure function of the shapes).
+ * Its first 256 KiB hold synchronisation counters: they must be zero before
+ * the buffer is first used (hipMemset once at allocation), and every call
+ * leaves them zero again, so one buffer serves any sequence of calls of any
+ * shapes, including calls captured in a HIP graph.  (The last 4 bytes of
+ * that region are a sticky flag, set to 1 if a workgroup ever stopped
+ * waiting and recomputed its input itself; results are the same either way.)
+ * The rest holds float32 partial sums and may contain anything.  Two calls
+ * that may run at the same time (e.g. on different streams) must not share
+ * a workspace.
  *
  * Aliasing.  y must not overlap x, v, the stacks or the workspace.
  *
@@ -94,6 +107,10 @@ int sgmv_abi_version(void);
 /* Human-readable name of a status code (static string, never NULL). */
 const char* sgmv_status_string(int status);
 
+/* Text of the last HIP error behind an SGMV_ERR_HIP returned to the calling
+ * thread ("no error" if there was none; static string, never NULL). */
+const char* sgmv_last_hip_error(void);
+
 /*
  * Shrink: v[i, :] = x[i, :] @ A_stack[adapter_ids[t]] for every row i of
  * every segment t (overwrite; float32).  Rows of v outside every segment
@@ -101,7 +118,7 @@ const char* sgmv_status_string(int status);
  * combined in a fixed order, so repeated calls give identical bits.
  *
  * workspace: device scratch of at least sgmv_shrink_workspace_bytes(...)
- * bytes (any contents; overwritten).  May be NULL only when that size is 0.
+ * bytes (see "Workspace" above).  May be NULL only when that size is 0.
  */
 size_t sgmv_shrink_workspace_bytes(int32_t num_rows, int32_t num_segments,
                                    int32_t H1, int32_t r, int32_t dtype);
@@ -126,8 +143,13 @@ int sgmv_expand(void* y, const float* v, const void* B_stack,
  * a = adapter_ids of row i's segment.  The intermediate v stays in float32
  * and never leaves the workspace.
  *
+ * Decode- and prefill-shaped calls with a vectorised rank run as a single
+ * kernel in which the expand workgroups wait, with bounded patience, for the
+ * shrink workgroups of their rows; the result does not depend on how long
+ * they wait.
+ *
  * workspace: device scratch of at least lora_apply_workspace_bytes(...)
- * bytes (any contents; overwritten).
+ * bytes (see "Workspace" above).
  */
 size_t lora_apply_workspace_bytes(int32_t num_rows, int32_t num_segments,
                                   int32_t H1, int32_t H2, int32_t r, int32_t dtype);
@@ -136,6 +158,17 @@ int lora_apply(void* y, const void* x, const void* A_stack, const void* B_stack,
                int32_t num_segments, int32_t num_rows, int32_t num_adapters,
                int32_t H1, int32_t H2, int32_t r, float scale, int32_t dtype,
                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Process-wide patience, in seconds (0 <= seconds <= 10; default 0.02), of
+ * the single-kernel lora_apply's expand workgroups waiting for their shrink
+ * workgroups.  A workgroup that stops waiting computes its input itself with
+ * the same arithmetic in the same order, so results never depend on this
+ * setting; 0 makes every expand workgroup do so without waiting (that is
+ * how the path is tested).  This is the library's only state.  Returns SGMV_OK or
+ * SGMV_ERR_BAD_SHAPE for a value out of range.
+ */
+int sgmv_set_fused_wait(double seconds);
 
 /*
  * Host-side check of a segment table held in HOST memory: seg_indptr

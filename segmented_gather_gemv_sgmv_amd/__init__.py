@@ -39,6 +39,7 @@ _i32, _sz, _vp, _f32 = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p, ctypes.
 ABI = [
     ("sgmv_abi_version", ctypes.c_int, []),
     ("sgmv_status_string", ctypes.c_char_p, [ctypes.c_int]),
+    ("sgmv_last_hip_error", ctypes.c_char_p, []),
     ("sgmv_shrink_workspace_bytes", _sz, [_i32, _i32, _i32, _i32, _i32]),
     ("sgmv_shrink", ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                    _vp, _sz, _vp]),
@@ -47,6 +48,7 @@ ABI = [
     ("lora_apply_workspace_bytes", _sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     ("lora_apply", ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                   _i32, _f32, _i32, _vp, _sz, _vp]),
+    ("sgmv_set_fused_wait", ctypes.c_int, [ctypes.c_double]),
     ("sgmv_validate_segments", ctypes.c_int, [_vp, _vp, _i32, _i32, _i32]),
 ]
 
@@ -62,10 +64,16 @@ _lib_lock = threading.Lock()
 
 
 def lib() -> ctypes.CDLL:
-    """The loaded ``libsgmv.so`` with argument types set (raises if not built)."""
+    """The loaded ``libsgmv.so`` with argument types set (raises if not built).
+
+    torch is imported first on purpose: torch ships its own HIP runtime
+    (soname libamdhip64.so.7), and the library must bind to that same
+    runtime so that torch's streams and allocations are valid in its calls.
+    Loaded the other way round, the process would hold two HIP runtimes."""
     global _lib_handle
     with _lib_lock:
         if _lib_handle is None:
+            import torch  # noqa: F401  (see above)
             if not os.path.exists(LIBRARY):
                 raise RuntimeError(
                     f"{LIBRARY} is missing: build it with "
@@ -81,6 +89,8 @@ def lib() -> ctypes.CDLL:
 
 def _check(code: int, what: str):
     if code != 0:
+        if code == 6:  # SGMV_ERR_HIP: add the HIP runtime's own message
+            what = f"{what} ({lib().sgmv_last_hip_error().decode()})"
         raise SGMVError(code, what)
 
 
@@ -124,8 +134,11 @@ def _segments(seg_indptr, adapter_ids, device):
 
 
 class _WorkspaceCache:
-    """One growable device buffer per (device, stream); calls on one stream
-    run in order, so reusing its buffer between them is safe."""
+    """One growable, zero-initialised device buffer per (device, stream).
+
+    Calls on one stream run in order, so they can share its buffer; the
+    library leaves the buffer's counter region zero after every call, as it
+    requires on entry."""
 
     def __init__(self):
         self._bufs = {}
@@ -137,7 +150,7 @@ class _WorkspaceCache:
         with self._lock:
             buf = self._bufs.get(key)
             if buf is None or buf.numel() < nbytes:
-                buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+                buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
                 self._bufs[key] = buf
             return buf
 
@@ -201,7 +214,11 @@ def sgmv_expand(y, v, B_stack, seg_indptr, adapter_ids, scale=1.0):
 
 
 def lora_apply(y, x, A_stack, B_stack, seg_indptr, adapter_ids, scale=1.0, workspace=None):
-    """y[i, :] += scale * (x[i, :] @ A_stack[a]) @ B_stack[a], fp32 accumulation."""
+    """y[i, :] += scale * (x[i, :] @ A_stack[a]) @ B_stack[a], fp32 accumulation.
+
+    ``workspace`` (optional): a uint8 device tensor of at least
+    ``lora_apply_workspace_bytes(...)`` bytes that was zero when first used
+    (e.g. ``torch.zeros``); by default a per-stream cached buffer is used."""
     dev = x.device
     _need(x, "x", dev, None, 2)
     _need(y, "y", dev, x.dtype, 2)
@@ -227,6 +244,11 @@ def lora_apply(y, x, A_stack, B_stack, seg_indptr, adapter_ids, scale=1.0, works
     return y
 
 
+def set_fused_wait(seconds: float) -> None:
+    """Patience of the single-kernel lora_apply's expand workgroups (see sgmv.h)."""
+    _check(lib().sgmv_set_fused_wait(float(seconds)), "sgmv_set_fused_wait")
+
+
 def validate_segments(seg_indptr, adapter_ids, num_rows, num_adapters) -> int:
     """Check a host (CPU) copy of a segment table; returns the status code."""
     import numpy as np
@@ -240,5 +262,5 @@ def validate_segments(seg_indptr, adapter_ids, num_rows, num_adapters) -> int:
 
 __all__ = [
     "lora_apply", "sgmv_shrink", "sgmv_expand", "lora_apply_workspace_bytes",
-    "shrink_workspace_bytes", "validate_segments", "lib", "SGMVError", "ABI", "LIBRARY",
+    "shrink_workspace_bytes", "validate_segments", "set_fused_wait", "lib", "SGMVError", "ABI", "LIBRARY",
 ]

@@ -9,11 +9,16 @@
 
 #include <stdint.h>
 
+#include <atomic>
+#include <cstring>
+#include <tuple>
 #include <type_traits>
+#include <utility>
 
 #include "sgmv.h"
 #include "sgmv_device.hpp"
 #include "sgmv_gemv.hpp"
+#include "sgmv_fused.hpp"
 
 namespace {
 
@@ -25,6 +30,12 @@ constexpr int kShrinkPG = 4;         // A loads in flight per lane
 constexpr int kExpandRows = 4;       // rows per expand tile
 constexpr int kGenericRows = 4;      // rows per tile in the general kernels
 constexpr int kGenericThreads = 256;
+constexpr int kFusedThreads = 256;   // threads per fused lora_apply workgroup
+constexpr int kFusedPG = 4;          // A loads in flight per lane (fused shrink)
+constexpr int kFusedItems = 1024;    // items that fit one resident wave (4 per CU)
+constexpr long long kFusedMaxChunk = 64 * 1024;  // largest A chunk per shrink item
+constexpr int kCompactMaxSegments = 1024;  // beyond: direct + overflow tile mapping
+constexpr double kDefaultWaitSeconds = 0.02;  // patience of a fused expand item
 constexpr int kTargetWorkgroups = 1024;  // at least four per CU on 256 CUs
 constexpr long long kMinChunkBytes = 4096;  // smallest A chunk worth a workgroup
 constexpr long long kMaxGrid = 0x7FFFFFFFLL;
@@ -81,8 +92,102 @@ Plan make_plan(int num_rows, int num_segments, int H1, int r, int dtype) {
     return p;
 }
 
+// Workspace layout shared by sgmv_shrink and lora_apply:
+//   [0, kCounterBytes)   counters of the fused kernel: one per tile slot,
+//                        kCounterStride ints apart (one 128-byte line each,
+//                        so atomics on different tiles do not contend), and a
+//                        sticky timeout flag in the last int.  Zero before
+//                        first use; every call leaves the tile counters at
+//                        zero.  The offset and size do not depend on the
+//                        shapes, so one buffer can serve calls of any shape.
+//   [kCounterBytes, ...) float32 chunk partials [ksplit][num_rows][r].
+constexpr int kCounterInts = 65536;
+constexpr int kCounterStride = 32;
+constexpr int kCounterSlots = kCounterInts / kCounterStride - 1;
+constexpr size_t kCounterBytes = kCounterInts * sizeof(int);
+
+// Launch plan of the single-kernel lora_apply (a pure function of shapes).
+struct FusedPlan {
+    bool ok;            // shapes allow it (alignment is checked per call)
+    int rows;           // tile rows: 1 when no segment needs more on average
+    int compact;        // compact tile mapping (block scan) vs direct + overflow
+    long long slots_a, slots_b;
+    int ksplit, h_per_split, csplit;
+    long long grid;
+};
+
+FusedPlan make_fused_plan(int num_rows, int num_segments, int H1, int H2, int r, int dtype) {
+    FusedPlan f{};
+    if (!vec_rank(dtype, r)) return f;
+    const int vec = vec_width(dtype);
+    f.rows = num_rows <= num_segments ? 1 : 4;
+    f.compact = num_segments <= kCompactMaxSegments;
+    if (f.compact) {
+        const long long m = num_segments < num_rows ? num_segments : num_rows;
+        f.slots_a = m + (num_rows - m) / f.rows;
+        f.slots_b = 0;
+    } else {
+        f.slots_a = num_segments;
+        f.slots_b = num_rows / f.rows;
+    }
+    const long long slots = f.slots_a + f.slots_b;
+    const int cw = kFusedThreads * vec;
+    f.csplit = (H2 + cw - 1) / cw;
+    // Split of the H1 reduction: as fine as fits one resident wave of items,
+    // but chunks between kMinChunkBytes and kFusedMaxChunk of A.
+    const long long a_bytes = (long long)H1 * r * elem_bytes(dtype);
+    long long hi = a_bytes / kMinChunkBytes;
+    if (hi < 1) hi = 1;
+    long long lo = 1;
+    while (lo * kFusedMaxChunk < a_bytes && lo < hi) lo *= 2;
+    long long k = 1;
+    while (k * 2 <= hi && slots * (k * 2 + f.csplit) <= kFusedItems) k *= 2;
+    if (k < lo) k = lo;
+    const int unit = kFusedThreads / (r / vec);
+    long long hps = (H1 + k - 1) / k;
+    hps = (hps + unit - 1) / unit * unit;
+    f.h_per_split = (int)hps;
+    f.ksplit = (int)((H1 + hps - 1) / hps);
+    f.grid = slots * (f.ksplit + f.csplit);
+    f.ok = slots <= kCounterSlots && f.ksplit < (1 << 16) && f.csplit < (1 << 15) &&
+           f.grid <= kMaxGrid;
+    return f;
+}
+
 size_t partial_bytes(const Plan& p, int num_rows, int r) {
     return (size_t)p.ksplit * (size_t)num_rows * (size_t)r * sizeof(float);
+}
+
+size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
+
+// Process-wide patience of the fused kernel's expand workgroups (seconds),
+// stored as the bits of a double so that it can be read without a lock.
+std::atomic<unsigned long long> g_wait_bits{0};
+
+double fused_wait_seconds() {
+    const unsigned long long b = g_wait_bits.load(std::memory_order_relaxed);
+    if (b == 0) return kDefaultWaitSeconds;
+    double d;
+    memcpy(&d, &b, sizeof d);
+    return d;
+}
+
+// Ticks of the constant-rate wall clock (wall_clock64) per second, per device.
+long long wall_ticks_per_second() {
+    static long long cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 100000000LL;
+    if (cache[dev] == 0) {
+        int khz = 0;
+        if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
+            khz <= 0) {
+            (void)hipGetLastError();  // do not leave our failed query to the caller
+            khz = 100000;
+        }
+        cache[dev] = (long long)khz * 1000LL;
+    }
+    return cache[dev];
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -94,9 +199,35 @@ int check_common(int num_segments, int num_rows, int num_adapters, int r, int dt
     return SGMV_OK;
 }
 
+// Launch bookkeeping: every launch goes through hipLaunchKernel, whose
+// return value describes that launch alone (hipGetLastError could also
+// report an older, unrelated error of the caller's).  The first failure of a
+// call is kept until launch_status() reads it; the last one stays readable
+// through sgmv_last_hip_error().
+thread_local hipError_t t_pending = hipSuccess;
+thread_local hipError_t t_last = hipSuccess;
+
+template <typename Tuple, size_t... I>
+void arg_pointers(Tuple& t, void** out, std::index_sequence<I...>) {
+    ((out[I] = (void*)&std::get<I>(t)), ...);
+}
+
+template <typename... KArgs, typename... Args>
+void launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t st, Args&&... args) {
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count mismatch");
+    std::tuple<std::decay_t<KArgs>...> vals(static_cast<std::decay_t<KArgs>>(args)...);
+    void* ptrs[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1];
+    arg_pointers(vals, ptrs, std::index_sequence_for<KArgs...>{});
+    const hipError_t e = hipLaunchKernel((const void*)kernel, grid, block, ptrs, 0, st);
+    if (e != hipSuccess && t_pending == hipSuccess) t_pending = e;
+}
+
 int launch_status() {
-    const hipError_t e = hipGetLastError();
-    return e == hipSuccess ? SGMV_OK : SGMV_ERR_HIP;
+    const hipError_t e = t_pending;
+    t_pending = hipSuccess;
+    if (e == hipSuccess) return SGMV_OK;
+    t_last = e;
+    return SGMV_ERR_HIP;
 }
 
 // -- shrink dispatch ---------------------------------------------------------
@@ -106,8 +237,7 @@ void launch_shrink_vec(float* out, long long out_stride, const void* x, const vo
                        const Plan& p, hipStream_t st) {
     using T = typename DT::storage;
     const unsigned grid = (unsigned)(tile_slots(S, rows, kShrinkRows) * p.ksplit);
-    hipLaunchKernelGGL((shrink_vec_kernel<DT, R, kShrinkThreads, kShrinkRows, kShrinkPG>),
-                       dim3(grid), dim3(kShrinkThreads), 0, st, out, out_stride,
+    launch(&shrink_vec_kernel<DT, R, kShrinkThreads, kShrinkRows, kShrinkPG>, dim3(grid), dim3(kShrinkThreads), st, out, out_stride,
                        (const T*)x, (const T*)A, seg, ids, S, rows, nad, H1, p.ksplit,
                        p.h_per_split);
 }
@@ -118,8 +248,8 @@ void launch_shrink_generic(float* out, long long out_stride, const void* x, cons
                            int H1, int r, const Plan& p, hipStream_t st) {
     using T = typename DT::storage;
     const unsigned grid = (unsigned)(tile_slots(S, rows, kGenericRows) * p.ksplit);
-    hipLaunchKernelGGL((shrink_generic_kernel<DT, kGenericThreads, kGenericRows>), dim3(grid),
-                       dim3(kGenericThreads), 0, st, out, out_stride, (const T*)x, (const T*)A,
+    launch(&shrink_generic_kernel<DT, kGenericThreads, kGenericRows>, dim3(grid),
+                       dim3(kGenericThreads), st, out, out_stride, (const T*)x, (const T*)A,
                        seg, ids, S, rows, nad, H1, r, p.ksplit, p.h_per_split);
 }
 
@@ -158,8 +288,7 @@ void launch_expand_vec(void* y, const float* vpart, long long v_stride, int P, c
     const int cw = kWave * DT::kVec;
     const int csplit = (H2 + cw - 1) / cw;
     const unsigned grid = (unsigned)(tile_slots(S, rows, kExpandRows) * csplit);
-    hipLaunchKernelGGL((expand_vec_kernel<DT, R, kExpandRows, KB>), dim3(grid), dim3(kWave), 0,
-                       st, (T*)y, vpart, v_stride, P, (const T*)B, seg, ids, S, rows, nad, H2,
+    launch(&expand_vec_kernel<DT, R, kExpandRows, KB>, dim3(grid), dim3(kWave), st, (T*)y, vpart, v_stride, P, (const T*)B, seg, ids, S, rows, nad, H2,
                        scale, csplit);
 }
 
@@ -170,8 +299,8 @@ void launch_expand_generic(void* y, const float* vpart, long long v_stride, int 
     using T = typename DT::storage;
     const int csplit = (H2 + kGenericThreads - 1) / kGenericThreads;
     const unsigned grid = (unsigned)(tile_slots(S, rows, kGenericRows) * csplit);
-    hipLaunchKernelGGL((expand_generic_kernel<DT, kGenericThreads, kGenericRows>), dim3(grid),
-                       dim3(kGenericThreads), 0, st, (T*)y, vpart, v_stride, P, (const T*)B, seg,
+    launch(&expand_generic_kernel<DT, kGenericThreads, kGenericRows>, dim3(grid),
+                       dim3(kGenericThreads), st, (T*)y, vpart, v_stride, P, (const T*)B, seg,
                        ids, S, rows, nad, r, H2, scale, csplit);
 }
 
@@ -227,6 +356,8 @@ extern "C" {
 
 int sgmv_abi_version(void) { return SGMV_ABI_VERSION; }
 
+const char* sgmv_last_hip_error(void) { return hipGetErrorString(t_last); }
+
 const char* sgmv_status_string(int status) {
     switch (status) {
         case SGMV_OK: return "ok";
@@ -245,14 +376,16 @@ size_t sgmv_shrink_workspace_bytes(int32_t num_rows, int32_t num_segments, int32
                                    int32_t dtype) {
     if (check_common(num_segments, num_rows, 0, r, dtype) != SGMV_OK || H1 < 1) return 0;
     const Plan p = make_plan(num_rows, num_segments, H1, r, dtype);
-    return p.ksplit > 1 ? partial_bytes(p, num_rows, r) : 0;
+    return p.ksplit > 1 ? kCounterBytes + partial_bytes(p, num_rows, r) : 0;
 }
 
 size_t lora_apply_workspace_bytes(int32_t num_rows, int32_t num_segments, int32_t H1, int32_t H2,
                                   int32_t r, int32_t dtype) {
     if (check_common(num_segments, num_rows, 0, r, dtype) != SGMV_OK || H1 < 1 || H2 < 1) return 0;
     const Plan p = make_plan(num_rows, num_segments, H1, r, dtype);
-    return partial_bytes(p, num_rows, r);
+    const FusedPlan f = make_fused_plan(num_rows, num_segments, H1, H2, r, dtype);
+    const int k = f.ok && f.ksplit > p.ksplit ? f.ksplit : p.ksplit;
+    return kCounterBytes + (size_t)k * (size_t)num_rows * (size_t)r * sizeof(float);
 }
 
 int sgmv_shrink(float* v, const void* x, const void* A_stack, const int32_t* seg_indptr,
@@ -266,10 +399,10 @@ int sgmv_shrink(float* v, const void* x, const void* A_stack, const int32_t* seg
     if (!v || !x || !A_stack || !seg_indptr || !adapter_ids) return SGMV_ERR_NULL_PTR;
     const Plan p = make_plan(num_rows, num_segments, H1, r, dtype);
     if (!grid_fits(p, 1)) return SGMV_ERR_UNSUPPORTED;
-    const size_t need = p.ksplit > 1 ? partial_bytes(p, num_rows, r) : 0;
+    const size_t need = p.ksplit > 1 ? kCounterBytes + partial_bytes(p, num_rows, r) : 0;
     if (need > 0 && (!workspace || workspace_bytes < need)) return SGMV_ERR_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
-    float* out = p.ksplit > 1 ? (float*)workspace : v;
+    float* out = p.ksplit > 1 ? (float*)((char*)workspace + kCounterBytes) : v;
     const long long stride = (long long)num_rows * r;
     with_dtype(dtype, [&](auto dt) {
         using DT = decltype(dt);
@@ -280,7 +413,7 @@ int sgmv_shrink(float* v, const void* x, const void* A_stack, const int32_t* seg
     if (p.ksplit > 1) {
         const long long n = stride;
         const unsigned grid = (unsigned)((n + 255) / 256);
-        hipLaunchKernelGGL(reduce_partials_kernel, dim3(grid), dim3(256), 0, st, v, out, stride,
+        launch(&reduce_partials_kernel, dim3(grid), dim3(256), st, v, out, stride,
                            p.ksplit, seg_indptr, adapter_ids, num_segments, num_rows,
                            num_adapters, r);
         rc = launch_status();
@@ -320,11 +453,51 @@ int lora_apply(void* y, const void* x, const void* A_stack, const void* B_stack,
     if (!y || !x || !A_stack || !B_stack || !seg_indptr || !adapter_ids) return SGMV_ERR_NULL_PTR;
     const Plan p = make_plan(num_rows, num_segments, H1, r, dtype);
     if (!grid_fits(p, H2)) return SGMV_ERR_UNSUPPORTED;
-    const size_t need = partial_bytes(p, num_rows, r);
+    const size_t need = lora_apply_workspace_bytes(num_rows, num_segments, H1, H2, r, dtype);
     if (!workspace || workspace_bytes < need) return SGMV_ERR_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
-    float* part = (float*)workspace;
+    int* counters = (int*)workspace;
+    float* part = (float*)((char*)workspace + kCounterBytes);
     const long long stride = (long long)num_rows * r;
+    const int vec = vec_width(dtype);
+    const bool aligned = aligned16(A_stack) && aligned16(B_stack) && aligned16(y);
+    const FusedPlan f = make_fused_plan(num_rows, num_segments, H1, H2, r, dtype);
+    const bool fused = f.ok && aligned && (H2 % vec == 0);
+    if (fused) {
+        const double wait_s = fused_wait_seconds();
+        const long long wait =
+            wait_s < 1e-300 ? -1 : (long long)(wait_s * (double)wall_ticks_per_second());
+        with_dtype(dtype, [&](auto dt) {
+            using DT = decltype(dt);
+            using T = typename DT::storage;
+            auto go = [&](auto rank, auto rows) {
+                constexpr int R = decltype(rank)::value;
+                constexpr int RB = decltype(rows)::value;
+                constexpr int KB = R < 16 ? R : 16;
+                launch(&lora_fused_kernel<DT, R, kFusedThreads, RB, kFusedPG, KB>,
+                       dim3((unsigned)f.grid), dim3(kFusedThreads), st, (T*)y, (const T*)x,
+                       (const T*)A_stack, (const T*)B_stack, seg_indptr, adapter_ids,
+                       num_segments, num_rows, num_adapters, H1, H2, scale, part, counters,
+                       f.ksplit, f.h_per_split, f.csplit, (int)f.slots_a, (int)f.slots_b,
+                       f.compact, kCounterInts, kCounterStride, wait);
+            };
+            auto by_rows = [&](auto rank) {
+                if (f.rows == 1) go(rank, std::integral_constant<int, 1>{});
+                else go(rank, std::integral_constant<int, 4>{});
+            };
+            switch (r) {
+                case 4:
+                    if constexpr (DT::kVec == 4) by_rows(std::integral_constant<int, 4>{});
+                    break;
+                case 8: by_rows(std::integral_constant<int, 8>{}); break;
+                case 16: by_rows(std::integral_constant<int, 16>{}); break;
+                case 32: by_rows(std::integral_constant<int, 32>{}); break;
+                case 64: by_rows(std::integral_constant<int, 64>{}); break;
+                default: by_rows(std::integral_constant<int, 128>{}); break;
+            }
+        });
+        return launch_status();
+    }
     with_dtype(dtype, [&](auto dt) {
         using DT = decltype(dt);
         dispatch_shrink<DT>(part, stride, x, A_stack, seg_indptr, adapter_ids, num_segments,
@@ -337,6 +510,21 @@ int lora_apply(void* y, const void* x, const void* A_stack, const void* B_stack,
                             num_segments, num_rows, num_adapters, r, H2, scale, p, st);
     });
     return launch_status();
+}
+
+int sgmv_set_fused_wait(double seconds) {
+    if (!(seconds >= 0.0) || seconds > 10.0) return SGMV_ERR_BAD_SHAPE;
+    unsigned long long b;
+    if (seconds == 0.0) {
+        // 0 must stay distinguishable from "unset": store the smallest
+        // positive double, which rounds to zero ticks.
+        const double tiny = 5e-324;
+        memcpy(&b, &tiny, sizeof b);
+    } else {
+        memcpy(&b, &seconds, sizeof b);
+    }
+    g_wait_bits.store(b, std::memory_order_relaxed);
+    return SGMV_OK;
 }
 
 int sgmv_validate_segments(const int32_t* h_seg_indptr, const int32_t* h_adapter_ids,

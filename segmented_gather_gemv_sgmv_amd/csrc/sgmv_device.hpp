@@ -235,4 +235,58 @@ __device__ __forceinline__ bool locate_tile(const int* __restrict__ seg_indptr,
     return true;
 }
 
+// Compact mapping: slot g is the g-th tile in segment order (all tiles of
+// segment 0, then of segment 1, ...), found with a block scan of the
+// per-segment tile counts.  A segment table with S segments over R rows has
+// at most m + floor((R - m) / T) tiles, m = min(S, R) (each non-empty
+// segment of n rows has 1 + floor((n - 1) / T) tiles), so a launch needs no
+// slot that finds nothing.  Every thread of the block must call this.
+template <int NT>
+__device__ __forceinline__ bool locate_tile_compact(const int* __restrict__ seg_indptr,
+                                                    const int* __restrict__ adapter_ids, int S,
+                                                    int num_rows, int num_adapters, int T, int g,
+                                                    int* lds, Tile& out) {
+    constexpr int NW = NT / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = threadIdx.x / kWave;
+    int* wave_tot = lds;            // [NW]
+    int* found = lds + NW;          // [0] = segment, [1] = tile index in segment
+    int running = 0;                // tiles in the segments already scanned
+    for (int base = 0; base < S; base += NT) {
+        const int s = base + (int)threadIdx.x;
+        int cnt = 0;
+        if (s < S) {
+            const SegBounds b = seg_bounds(seg_indptr, adapter_ids, s, num_rows, num_adapters);
+            if (b.ok) cnt = (b.hi - b.lo + T - 1) / T;
+        }
+        const int incl_w = wave_inclusive_scan(cnt, lane);
+        if (lane == kWave - 1) wave_tot[wid] = incl_w;
+        __syncthreads();
+        int off = 0, total = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const int t = wave_tot[w];
+            off += (w < wid) ? t : 0;
+            total += t;
+        }
+        const int excl = running + off + incl_w - cnt;
+        // Exactly one thread owns tile g if it lies in this pass.
+        if (cnt > 0 && g >= excl && g < excl + cnt) {
+            found[0] = s;
+            found[1] = g - excl;
+        }
+        running += total;
+        __syncthreads();  // found[] visible; wave_tot[] free for the next pass
+        if (g < running) break;  // block-uniform
+    }
+    if (g >= running) return false;  // fewer tiles than g + 1
+    const int s = found[0];
+    const SegBounds b = seg_bounds(seg_indptr, adapter_ids, s, num_rows, num_adapters);
+    out.seg = s;
+    out.row0 = b.lo + found[1] * T;
+    out.nrows = min(T, b.hi - out.row0);
+    out.adapter = adapter_ids[s];
+    return true;
+}
+
 }  // namespace sgmv

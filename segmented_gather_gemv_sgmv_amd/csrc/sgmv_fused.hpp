@@ -1,0 +1,360 @@
+// sgmv_fused.hpp -- lora_apply in one launch: shrink and expand of every
+// segment tile, with the float32 intermediate handed from the shrink
+// workgroups to the expand workgroups through the workspace.
+//
+// Why one launch: a decode-shaped call moves only tens of MB, so a second
+// launch (and the drain and ramp around it) costs as much as the data; the
+// expand workgroups also start streaming their B and y while the shrink is
+// still running (the pages stress that fusing the gather-multiply avoids
+// kernel-launch overhead: Punica walkthrough, omica.com.cn/news/959180,
+// section 2.2).
+//
+// Items.  Workgroup b < slots*ksplit is shrink item (tile g, H1 chunk p): it
+// writes the chunk's partial sums of v for the tile rows, then adds one to
+// the tile's arrival counter (release, agent scope).  Workgroup b beyond is
+// expand item (tile g, column chunk c): it issues its B and y loads, waits
+// until the tile's counter reaches ksplit (acquire, agent scope), sums the
+// partials in chunk order and updates y.
+//
+// Progress.  Shrink items never wait, and a workgroup's index is below every
+// expand index, so on hardware that dispatches each XCD's workgroups in index
+// order the waits always end.  The wait is nevertheless bounded in time; a
+// workgroup that runs out of patience computes the tile's partials itself
+// with the same code and in the same order, so the result is bit-identical
+// either way and the kernel never hangs.
+//
+// Hand-off without L2 write-backs.  A release fence at agent scope writes
+// back the whole L2 of the XCD and costs microseconds per workgroup, so the
+// partials never sit in L2 as plain data: they are written with agent-scope
+// atomic stores (write-through to the device coherence point), every wave
+// waits until its stores are acknowledged (s_waitcnt vmcnt(0)) before the
+// workgroup barrier, and only then does thread 0 bump the arrival counter.
+// Readers poll the counter and read the partials with agent-scope atomic
+// loads, which are served from the coherence point and never from a stale
+// cache line.  Every access to shared data is thus coherent at agent scope,
+// and the counter is published only after the data it announces.
+//
+// Counters.  counters[g * counter_stride] of tile slot g (one cache line per
+// tile, so that atomics of different tiles do not contend) counts the
+// tile's participants: each
+// of its ksplit shrink items adds 1 once its partials are stored, each of
+// its csplit expand items adds 1 << 16 once it no longer needs the
+// partials.  Expand items wait for the low half to reach ksplit.  The
+// participant whose addition completes the count (ksplit + csplit << 16)
+// returns the counter to zero, so the workspace is ready for the next call
+// (and for a graph replay) without a memset; it must be zero before its
+// first use.  Because every participant counts, a late shrink item (one
+// whose expand items stopped waiting) still finishes before the reset.  One
+// counter per tile keeps same-address atomics to ksplit + csplit per call
+// (cross-XCD atomics on one address serialise).  counters[n_counters-1] is
+// a sticky flag recording that some expand item stopped waiting.
+#pragma once
+
+#include "sgmv_device.hpp"
+#include "sgmv_gemv.hpp"
+
+namespace sgmv {
+
+// One H1 chunk of the shrink for one tile, reduced across the workgroup.
+// Calls emit(i, k, value) once for every (row i < nrows, column k < R), from
+// threads tid < R * RB; the values are bit-identical for identical inputs.
+// The caller must synchronise the block before s_red is used again.
+template <typename DT, int R, int NT, int RB, int PG, typename Emit>
+__device__ __forceinline__ void shrink_chunk(const typename DT::storage* __restrict__ A,
+                                             const typename DT::storage* __restrict__ xr,
+                                             int nrows, int H1, int h_lo, int h_hi,
+                                             float* s_red, Emit&& emit) {
+    constexpr int VEC = DT::kVec;
+    constexpr int LPR = R / VEC;
+    constexpr int HPB = NT / LPR;
+    constexpr int NW = NT / kWave;
+    constexpr int N = RB * VEC;
+    using RS = ReduceScatter<N, LPR>;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wid = tid / kWave;
+    const int h_lane = tid / LPR;
+    const int k0 = (tid % LPR) * VEC;
+
+    float acc[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc[i] = 0.f;
+
+    for (int hb = h_lo; hb < h_hi; hb += HPB * PG) {
+        uint4 av[PG];
+        float xv[PG][RB];
+#pragma unroll
+        for (int q = 0; q < PG; ++q) {
+            const int h = hb + q * HPB + h_lane;
+            const bool in = h < h_hi;
+            av[q] = in ? load16(A + (long long)h * R + k0) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < RB; ++i)
+                xv[q][i] = (in && i < nrows) ? DT::load1(xr + (long long)i * H1 + h) : 0.f;
+        }
+#pragma unroll
+        for (int q = 0; q < PG; ++q) {
+            float af[VEC];
+            DT::unpack(av[q], af);
+#pragma unroll
+            for (int i = 0; i < RB; ++i) {
+                if (i < nrows) {
+#pragma unroll
+                    for (int c = 0; c < VEC; ++c)
+                        acc[i * VEC + c] = fmaf(xv[q][i], af[c], acc[i * VEC + c]);
+                }
+            }
+        }
+    }
+
+    int offset;
+    bool canon;
+    RS::run(acc, lane, offset, canon);
+    if (canon) {
+        const int kq = lane % LPR;
+#pragma unroll
+        for (int i = 0; i < RS::kRemain; ++i) s_red[wid * (LPR * N) + kq * N + offset + i] = acc[i];
+    }
+    __syncthreads();
+    for (int t = tid; t < LPR * N; t += NT) {
+        const int kq = t / N;
+        const int idx = t - kq * N;
+        const int i = idx / VEC;
+        const int k = kq * VEC + (idx - i * VEC);
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) sum += s_red[w * (LPR * N) + t];
+        if (i < nrows) emit(i, k, sum);
+    }
+}
+
+// Adds `amount` to a tile counter; the participant that completes `total`
+// returns the counter to zero.  The wait makes the workgroup's earlier
+// memory operations (partial stores, poll loads) complete first.
+__device__ __forceinline__ void depart(int* counter, int amount, int total) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    const int before = __hip_atomic_fetch_add(counter, amount, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    if (before + amount == total)
+        __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename DT, int R, int NT, int RB, int PG, int KB>
+__global__ __launch_bounds__(NT) void lora_fused_kernel(
+    typename DT::storage* __restrict__ y, const typename DT::storage* __restrict__ x,
+    const typename DT::storage* __restrict__ A_stack,
+    const typename DT::storage* __restrict__ B_stack, const int* __restrict__ seg_indptr,
+    const int* __restrict__ adapter_ids, int S, int num_rows, int num_adapters, int H1, int H2,
+    float scale, float* __restrict__ partials, int* __restrict__ counters, int ksplit,
+    int h_per_split, int csplit, int slots_a, int slots_b, int compact, int n_counters,
+    int counter_stride, long long wait_ticks) {
+    using st = typename DT::storage;
+    constexpr int VEC = DT::kVec;
+    constexpr int CW = NT * VEC;  // columns per expand item
+    constexpr int NW = NT / kWave;
+    constexpr int LPR = R / VEC;
+    constexpr int N = RB * VEC;
+    static_assert(R % KB == 0, "KB must divide R");
+
+    __shared__ int s_scan[NT / kWave + 4];
+    __shared__ float s_red[NW * LPR * N];
+    __shared__ float s_v[RB * R];
+    __shared__ int s_flag;
+
+    const int tid = threadIdx.x;
+    const long long row_stride = (long long)num_rows * R;  // between chunk partials
+
+    // Items in launch order: shrink then expand items of the slots_a first
+    // slots, then shrink then expand items of the slots_b remaining ones.
+    // Every expand item thus follows all shrink items of its tile.
+    long long item = blockIdx.x;
+    int base = 0, nslots = slots_a;
+    if (item >= (long long)slots_a * (ksplit + csplit)) {
+        item -= (long long)slots_a * (ksplit + csplit);
+        base = slots_a;
+        nslots = slots_b;
+    }
+    const long long n_shrink = (long long)nslots * ksplit;
+    auto locate = [&](int g, Tile& t) {
+        return compact ? locate_tile_compact<NT>(seg_indptr, adapter_ids, S, num_rows,
+                                                 num_adapters, RB, g, s_scan, t)
+                       : locate_tile<NT>(seg_indptr, adapter_ids, S, num_rows, num_adapters,
+                                         RB, g, s_scan, t);
+    };
+
+    if (item < n_shrink) {
+        // ---------------- shrink item ----------------
+        const int g = base + (int)(item / ksplit);
+        const int p = (int)(item % ksplit);
+        Tile tile;
+        if (locate(g, tile)) {
+            const int h_lo = p * h_per_split;
+            const int h_hi = min(H1, h_lo + h_per_split);
+            const st* A = A_stack + (long long)tile.adapter * H1 * R;
+            const st* xr = x + (long long)tile.row0 * H1;
+            float* out = partials + (long long)p * row_stride + (long long)tile.row0 * R;
+            shrink_chunk<DT, R, NT, RB, PG>(
+                A, xr, tile.nrows, H1, h_lo, h_hi, s_red, [&](int i, int k, float v) {
+                    __hip_atomic_store(&out[i * R + k], v, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                });
+            // Each wave waits for its partial stores to be acknowledged; the
+            // barrier then lets thread 0 announce them.
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (tid == 0) depart(&counters[g * counter_stride], 1, ksplit + (csplit << 16));
+        }
+    } else {
+        // ---------------- expand item ----------------
+        const long long e = item - n_shrink;
+        const int g = base + (int)(e / csplit);
+        const int c = (int)(e % csplit);
+        Tile tile;
+        if (locate(g, tile)) {
+            const int nrows = tile.nrows;
+            const int j = c * CW + tid * VEC;
+            const bool active = j < H2;
+            const st* B = B_stack + (long long)tile.adapter * R * H2 + j;
+
+            // Loads that do not depend on v go out before the wait.
+            uint4 bv[KB];
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk)
+                bv[kk] = active ? load16(B + (long long)kk * H2) : make_uint4(0, 0, 0, 0);
+            uint4 yv[RB];
+#pragma unroll
+            for (int i = 0; i < RB; ++i)
+                yv[i] = (active && i < nrows)
+                            ? load16(y + (long long)(tile.row0 + i) * H2 + j)
+                            : make_uint4(0, 0, 0, 0);
+
+            if (tid == 0) {
+                // Poll with relaxed loads (no cache invalidation per poll);
+                // one acquire fence once the count is complete.
+                int ok = wait_ticks >= 0;  // negative: take the self-contained path
+                int* cnt = &counters[g * counter_stride];
+                if (ok && (__hip_atomic_load(cnt, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT) & 0xFFFF) < ksplit) {
+                    // Bounded by the wall clock and, independently, by a count
+                    // of polls (each poll sleeps >= 128 cycles), so the loop
+                    // ends even if the clock were to stand still.
+                    const long long t0 = wall_clock64();
+                    for (int polls = 0;; ++polls) {
+                        if ((__hip_atomic_load(cnt, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT) & 0xFFFF) >= ksplit)
+                            break;
+                        if (wall_clock64() - t0 > wait_ticks || polls >= (1 << 22)) {
+                            ok = 0;
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(2);
+                    }
+                }
+                s_flag = ok;
+            }
+            __syncthreads();
+            const bool ready = s_flag != 0;
+
+            if (ready) {
+                for (int t = tid; t < RB * R; t += NT) {
+                    const int i = t / R;
+                    const int k = t - i * R;
+                    float sum = 0.f;
+                    if (i < nrows) {
+                        float* vp = partials + (long long)(tile.row0 + i) * R + k;
+                        // Batches of loads in flight, summed in chunk order.
+                        for (int p0 = 0; p0 < ksplit; p0 += 8) {
+                            float tv[8];
+#pragma unroll
+                            for (int u = 0; u < 8; ++u)
+                                tv[u] = (p0 + u < ksplit)
+                                            ? __hip_atomic_load(vp + (long long)(p0 + u) * row_stride,
+                                                                __ATOMIC_RELAXED,
+                                                                __HIP_MEMORY_SCOPE_AGENT)
+                                            : 0.f;
+#pragma unroll
+                            for (int u = 0; u < 8; ++u)
+                                if (p0 + u < ksplit) sum += tv[u];
+                        }
+                    }
+                    s_v[t] = sum;
+                }
+            } else {
+                // The producers are late: compute every chunk here, summing in
+                // the same order as the normal path.
+                if (tid == 0) __hip_atomic_store(&counters[n_counters - 1], 1, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+                for (int t = tid; t < RB * R; t += NT) s_v[t] = 0.f;
+                __syncthreads();
+                const st* A = A_stack + (long long)tile.adapter * H1 * R;
+                const st* xr = x + (long long)tile.row0 * H1;
+                for (int pp = 0; pp < ksplit; ++pp) {
+                    const int h_lo = pp * h_per_split;
+                    const int h_hi = min(H1, h_lo + h_per_split);
+                    shrink_chunk<DT, R, NT, RB, PG>(A, xr, nrows, H1, h_lo, h_hi, s_red,
+                                                    [&](int i, int k, float v) { s_v[i * R + k] += v; });
+                    __syncthreads();
+                }
+                // Load B and y again, so that the prefetched registers are not
+                // held across this rarely taken path.
+#pragma unroll
+                for (int kk = 0; kk < KB; ++kk)
+                    bv[kk] = active ? load16(B + (long long)kk * H2) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < RB; ++i)
+                    yv[i] = (active && i < nrows)
+                                ? load16(y + (long long)(tile.row0 + i) * H2 + j)
+                                : make_uint4(0, 0, 0, 0);
+            }
+            __syncthreads();
+            // The partials are in LDS now: this item no longer needs them.
+            if (tid == 0) depart(&counters[g * counter_stride], 1 << 16, ksplit + (csplit << 16));
+
+            float acc[RB][VEC];
+#pragma unroll
+            for (int i = 0; i < RB; ++i)
+#pragma unroll
+                for (int q = 0; q < VEC; ++q) acc[i][q] = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < R; kb += KB) {
+                if (kb > 0) {
+#pragma unroll
+                    for (int kk = 0; kk < KB; ++kk)
+                        bv[kk] = active ? load16(B + (long long)(kb + kk) * H2)
+                                        : make_uint4(0, 0, 0, 0);
+                }
+#pragma unroll
+                for (int kk = 0; kk < KB; ++kk) {
+                    float bf[VEC];
+                    DT::unpack(bv[kk], bf);
+#pragma unroll
+                    for (int i = 0; i < RB; ++i) {
+                        if (i < nrows) {
+                            const float vv = s_v[i * R + kb + kk];
+#pragma unroll
+                            for (int q = 0; q < VEC; ++q) acc[i][q] = fmaf(vv, bf[q], acc[i][q]);
+                        }
+                    }
+                }
+            }
+            if (active) {
+#pragma unroll
+                for (int i = 0; i < RB; ++i) {
+                    if (i < nrows) {
+                        float yf[VEC];
+                        DT::unpack(yv[i], yf);
+#pragma unroll
+                        for (int q = 0; q < VEC; ++q) yf[q] = fmaf(scale, acc[i][q], yf[q]);
+                        store16(y + (long long)(tile.row0 + i) * H2 + j, DT::pack(yf));
+                    }
+                }
+            }
+        }
+    }
+
+    // ---------------- completion: the last workgroup resets the counters ----
+}
+
+}  // namespace sgmv

@@ -20,6 +20,21 @@
 
 namespace sgmv {
 
+// Sum of P chunk partials p[0], p[stride], ..., in chunk order, with the
+// loads issued in batches so that they are in flight together.
+__device__ __forceinline__ float sum_partials(const float* __restrict__ p, long long stride, int P) {
+    float sum = 0.f;
+    for (int p0 = 0; p0 < P; p0 += 8) {
+        float t[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) t[u] = (p0 + u < P) ? p[(long long)(p0 + u) * stride] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (p0 + u < P) sum += t[u];
+    }
+    return sum;
+}
+
 // ---------------------------------------------------------------------------
 // Wave reduce-scatter.  Each lane holds N floats; lanes whose ids differ only
 // in the bits LPR, 2*LPR, ..., 32 hold partial sums of the same N quantities.
@@ -214,10 +229,7 @@ __global__ __launch_bounds__(kWave) void expand_vec_kernel(
         const int i = t / R;
         const int k = t - i * R;
         float sum = 0.f;
-        if (i < nrows) {
-            const float* vp = vpart + (long long)(tile.row0 + i) * R + k;
-            for (int pp = 0; pp < P; ++pp) sum += vp[(long long)pp * v_stride];
-        }
+        if (i < nrows) sum = sum_partials(vpart + (long long)(tile.row0 + i) * R + k, v_stride, P);
         s_v[i][k] = sum;
     }
     __syncthreads();
@@ -339,10 +351,7 @@ __global__ __launch_bounds__(NT) void expand_generic_kernel(
         const int i = t / r;
         const int k = t - i * r;
         float sum = 0.f;
-        if (i < tile.nrows) {
-            const float* vp = vpart + (long long)(tile.row0 + i) * r + k;
-            for (int pp = 0; pp < P; ++pp) sum += vp[(long long)pp * v_stride];
-        }
+        if (i < tile.nrows) sum = sum_partials(vpart + (long long)(tile.row0 + i) * r + k, v_stride, P);
         s_v[t] = sum;
     }
     __syncthreads();
@@ -387,9 +396,7 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(
     }
     const SegBounds b = seg_bounds(seg_indptr, adapter_ids, lo, num_rows, num_adapters);
     if (!b.ok || row < b.lo || row >= b.hi) return;
-    float sum = 0.f;
-    for (int pp = 0; pp < P; ++pp) sum += vpart[(long long)pp * v_stride + e];
-    v[e] = sum;
+    v[e] = sum_partials(vpart + e, v_stride, P);
 }
 
 }  // namespace sgmv

@@ -213,7 +213,7 @@ def test_graph_replay_matches_eager():
     w = wl.config(2)
     d = to_device(w)
     y_eager = torch.from_numpy(gpu_lora_apply(w, d))
-    ws = torch.empty(sg.lora_apply_workspace_bytes(w.num_rows, w.num_segments, w.H1, w.H2, w.r,
+    ws = torch.zeros(sg.lora_apply_workspace_bytes(w.num_rows, w.num_segments, w.H1, w.H2, w.r,
                                                    torch_dtype(w.dtype)),
                      dtype=torch.uint8, device="cuda")
     y = d["y0"].clone()
@@ -233,3 +233,81 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         assert torch.equal(y.double().cpu(), y_eager), f"replay {rep}"
         del junk
+
+
+@pytest.mark.parametrize("cfg", [(2, True), (4, False), (3, False)],
+                         ids=["skewed_control", "mlp_up", "prefill"])
+def test_fused_self_contained_path_is_bit_identical(cfg):
+    """With zero patience every expand workgroup of the split hand-off
+    kernel recomputes its rows' partial sums itself; the output must be
+    bit-identical to the normal hand-off path, and the sticky flag is set."""
+    import torch
+    import segmented_gather_gemv_sgmv_amd as sg
+    w = wl.config(cfg[0], control=cfg[1])
+    d = to_device(w)
+    ws = torch.zeros(sg.lora_apply_workspace_bytes(w.num_rows, w.num_segments, w.H1, w.H2, w.r,
+                                                   torch_dtype(w.dtype)),
+                     dtype=torch.uint8, device="cuda")
+
+    def run():
+        y = d["y0"].clone()
+        sg.lora_apply(y, d["x"], d["A"], d["B"], d["seg"], d["ids"], w.scale, workspace=ws)
+        torch.cuda.synchronize()
+        return y
+
+    normal = run()
+    counters = ws[:262144].view(torch.int32)
+    assert int(counters[-1]) == 0 and int(counters[:-1].abs().sum()) == 0
+    try:
+        sg.set_fused_wait(0.0)
+        alone = run()
+    finally:
+        sg.set_fused_wait(0.02)
+    assert torch.equal(normal, alone)
+    assert int(counters[-1]) == 1, "the self-contained path did not run"
+    assert int(counters[:-1].abs().sum()) == 0, "counters not returned to zero"
+
+
+def test_workspace_reused_across_shapes():
+    """One workspace serves calls of different shapes in any order (the
+    counters sit at a fixed offset and are left at zero)."""
+    import torch
+    import segmented_gather_gemv_sgmv_amd as sg
+    shapes = [(0, "f16", 4096, 4096, 16, 64, 64, 64), (1, "bf16", 1024, 3072, 64, 9, 200, 40),
+              (2, "f16", 2048, 1024, 8, 5, 30, 3), (3, "f32", 512, 768, 16, 7, 300, 90)]
+    work = [wl.small_random(sd, dt, H1, H2, r, N, R, S) for sd, dt, H1, H2, r, N, R, S in shapes]
+    need = max(sg.lora_apply_workspace_bytes(w.num_rows, w.num_segments, w.H1, w.H2, w.r,
+                                             torch_dtype(w.dtype)) for w in work)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for w in work + work[::-1] + work:
+        d = to_device(w)
+        y = d["y0"].clone()
+        sg.lora_apply(y, d["x"], d["A"], d["B"], d["seg"], d["ids"], w.scale, workspace=ws)
+        torch.cuda.synchronize()
+        y_ref, _ = oracle.lora_apply(w.y0, w.x, w.A, w.B, w.seg_indptr, w.adapter_ids, w.scale)
+        assert_close(y.double().cpu().numpy(), y_ref, w.dtype, w.name)
+        assert int(ws[:262144].view(torch.int32).abs().sum()) == 0
+
+
+@pytest.mark.parametrize("S,R,lengths_kind", [(1500, 1500, "ones"), (1300, 700, "sparse"),
+                                              (40, 160, "mixed")])
+def test_tile_mappings(S, R, lengths_kind):
+    """Decode-shaped batches through the single-kernel lora_apply: the direct
+    tile mapping (more than 1024 segments), the compact mapping with many
+    empty segments, and tiles of four rows."""
+    rng = np.random.default_rng(S + R)
+    if lengths_kind == "ones":
+        lengths = [1] * S
+    elif lengths_kind == "sparse":
+        lengths = [0] * S
+        for i in rng.choice(S, size=R, replace=True):
+            lengths[i] += 1
+    else:
+        lengths = list(rng.integers(0, 9, size=S))
+        lengths[-1] += R - sum(lengths)
+    ids = rng.integers(0, 24, size=S)
+    w = wl.make_workload("decode_map", "f16", 1024, 1536, 16, 24, lengths, ids, 0.75,
+                         seed=S, num_rows=R)
+    assert w.seg_indptr[-1] <= R
+    y_ref, _ = oracle.lora_apply(w.y0, w.x, w.A, w.B, w.seg_indptr, w.adapter_ids, w.scale)
+    assert_close(gpu_lora_apply(w), y_ref, "f16", f"decode mapping {lengths_kind}")
