@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark: SGMV LoRA add-on (lora_apply) on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--report FILE]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
 
 Workload: Llama-2-7B decode projection, H1 = H2 = 4096, r = 16, 64 rows in
 64 one-row segments (a distinct adapter per row), fp16 with fp32
@@ -127,6 +127,49 @@ def run_gpu(w, steps: int, warmup: int, device="cuda:0"):
     return dict(gpu_ms=gpu_ms, wall_s=wall, nsets=nsets, per_set_bytes=per_set)
 
 
+KERNEL_SOURCES = ("segmented_gather_gemv_sgmv_amd/csrc/sgmv_api.hip",
+                  "segmented_gather_gemv_sgmv_amd/csrc/sgmv_fused.hpp",
+                  "segmented_gather_gemv_sgmv_amd/csrc/sgmv_gemv.hpp",
+                  "segmented_gather_gemv_sgmv_amd/csrc/sgmv_device.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_lora_fused_kernel_llama7b_decode.json")
+
+
+def kernel_source_hash() -> str:
+    """SHA-256 over the HIP sources the measured kernel is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload_name: str):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE and
+    WRITE_SIZE counts (scaled by the copy-kernel calibration), or None when
+    they were taken on other kernel sources or another workload."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != kernel_source_hash() or t.get("workload") != workload_name:
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def copy_calibration(nbytes: int, reps: int = 20):
+    """A plain device-to-device copy of known size, for scaling the
+    FETCH_SIZE / WRITE_SIZE counters (run it under rocprofv3 --pmc)."""
+    import torch
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
+
+
 def cpu_baseline(w, budget_s: float = 10.0):
     """The CPU oracle (single thread, plain fp64 loops) on the same batch."""
     import oracle
@@ -152,8 +195,12 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--report", default=None, help="append per-workload JSON lines to FILE")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain BYTES-sized device copy (counter calibration)")
     args = ap.parse_args(argv)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
@@ -202,7 +249,7 @@ def main(argv=None):
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": None,
+            "traffic": measured_traffic(w.name),
             "algorithmic_bytes_per_launch": abytes,
             "tflops": flops / step_s / 1e12,
         },
