@@ -19,6 +19,7 @@
 #include "sgmv_device.hpp"
 #include "sgmv_gemv.hpp"
 #include "sgmv_fused.hpp"
+#include "sgmv_mfma.hpp"
 
 namespace {
 
@@ -152,6 +153,55 @@ FusedPlan make_fused_plan(int num_rows, int num_segments, int H1, int H2, int r,
     f.ok = slots <= kCounterSlots && f.ksplit < (1 << 16) && f.csplit < (1 << 15) &&
            f.grid <= kMaxGrid;
     return f;
+}
+
+// Launch plan of the MFMA row-tile kernel (16-row tiles, fp16/bf16, r a
+// multiple of 16): chosen when segments hold several rows on average, where
+// the two contractions are dense enough for the matrix cores.
+constexpr int kMfmaRowsPerSegment = 4;  // use MFMA tiles when R >= 4 S
+struct MfmaPlan {
+    bool ok;
+    int compact;
+    long long slots_a, slots_b;
+    int ksplit, h_per_split, csplit;
+    long long grid;
+};
+
+MfmaPlan make_mfma_plan(int num_rows, int num_segments, int H1, int H2, int r, int dtype) {
+    MfmaPlan f{};
+    if (dtype == SGMV_F32 || (r != 16 && r != 32 && r != 64 && r != 128)) return f;
+    if (H1 % 8 != 0 || H2 % 8 != 0) return f;
+    constexpr int T = 16;
+    f.compact = num_segments <= kCompactMaxSegments;
+    if (f.compact) {
+        const long long m = num_segments < num_rows ? num_segments : num_rows;
+        f.slots_a = m + (num_rows - m) / T;
+        f.slots_b = 0;
+    } else {
+        f.slots_a = num_segments;
+        f.slots_b = num_rows / T;
+    }
+    const long long slots = f.slots_a + f.slots_b;
+    const int kc_max = 16384 / r;
+    const int cw = (8192 / r) < 512 ? (8192 / r) : 512;
+    f.csplit = (H2 + cw - 1) / cw;
+    // Fewest chunks that fit the LDS copy of A, more while items still fit
+    // one resident wave and chunks keep at least 256 rows of A.
+    long long k = (H1 + kc_max - 1) / kc_max;
+    while (H1 / (k * 2) >= 256 && slots * (k * 2 + f.csplit) <= kFusedItems) k *= 2;
+    long long hps = (H1 + k - 1) / k;
+    hps = (hps + 127) / 128 * 128;
+    if (hps > kc_max) hps = kc_max;
+    f.h_per_split = (int)hps;
+    f.ksplit = (int)((H1 + hps - 1) / hps);
+    f.grid = slots * (f.ksplit + f.csplit);
+    f.ok = slots <= kCounterSlots && f.ksplit < (1 << 16) && f.csplit < (1 << 15) &&
+           f.grid <= kMaxGrid;
+    return f;
+}
+
+bool use_mfma(int num_rows, int num_segments) {
+    return (long long)num_rows >= (long long)kMfmaRowsPerSegment * num_segments;
 }
 
 size_t partial_bytes(const Plan& p, int num_rows, int r) {
@@ -384,7 +434,10 @@ size_t lora_apply_workspace_bytes(int32_t num_rows, int32_t num_segments, int32_
     if (check_common(num_segments, num_rows, 0, r, dtype) != SGMV_OK || H1 < 1 || H2 < 1) return 0;
     const Plan p = make_plan(num_rows, num_segments, H1, r, dtype);
     const FusedPlan f = make_fused_plan(num_rows, num_segments, H1, H2, r, dtype);
-    const int k = f.ok && f.ksplit > p.ksplit ? f.ksplit : p.ksplit;
+    const MfmaPlan mp = make_mfma_plan(num_rows, num_segments, H1, H2, r, dtype);
+    int k = p.ksplit;
+    if (f.ok && f.ksplit > k) k = f.ksplit;
+    if (mp.ok && mp.ksplit > k) k = mp.ksplit;
     return kCounterBytes + (size_t)k * (size_t)num_rows * (size_t)r * sizeof(float);
 }
 
@@ -461,12 +514,36 @@ int lora_apply(void* y, const void* x, const void* A_stack, const void* B_stack,
     const long long stride = (long long)num_rows * r;
     const int vec = vec_width(dtype);
     const bool aligned = aligned16(A_stack) && aligned16(B_stack) && aligned16(y);
+    const double wait_s = fused_wait_seconds();
+    const long long wait =
+        wait_s < 1e-300 ? -1 : (long long)(wait_s * (double)wall_ticks_per_second());
+    const MfmaPlan mp = make_mfma_plan(num_rows, num_segments, H1, H2, r, dtype);
+    if (mp.ok && aligned && aligned16(x) && use_mfma(num_rows, num_segments)) {
+        auto go = [&](auto dt, auto rank) {
+            using DT = decltype(dt);
+            using T = typename DT::storage;
+            constexpr int R = decltype(rank)::value;
+            launch(&lora_mfma_kernel<DT, R>, dim3((unsigned)mp.grid), dim3(256), st, (T*)y,
+                   (const T*)x, (const T*)A_stack, (const T*)B_stack, seg_indptr, adapter_ids,
+                   num_segments, num_rows, num_adapters, H1, H2, scale, part, counters,
+                   mp.ksplit, mp.h_per_split, mp.csplit, (int)mp.slots_a, (int)mp.slots_b,
+                   mp.compact, kCounterInts, kCounterStride, wait);
+        };
+        auto by_rank = [&](auto dt) {
+            switch (r) {
+                case 16: go(dt, std::integral_constant<int, 16>{}); break;
+                case 32: go(dt, std::integral_constant<int, 32>{}); break;
+                case 64: go(dt, std::integral_constant<int, 64>{}); break;
+                default: go(dt, std::integral_constant<int, 128>{}); break;
+            }
+        };
+        if (dtype == SGMV_F16) by_rank(F16{});
+        else by_rank(BF16{});
+        return launch_status();
+    }
     const FusedPlan f = make_fused_plan(num_rows, num_segments, H1, H2, r, dtype);
     const bool fused = f.ok && aligned && (H2 % vec == 0);
     if (fused) {
-        const double wait_s = fused_wait_seconds();
-        const long long wait =
-            wait_s < 1e-300 ? -1 : (long long)(wait_s * (double)wall_ticks_per_second());
         with_dtype(dtype, [&](auto dt) {
             using DT = decltype(dt);
             using T = typename DT::storage;

@@ -140,6 +140,79 @@ __device__ __forceinline__ void depart(int* counter, int amount, int total) {
         __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Thread 0 of an expand item: waits until the tile's ksplit shrink items
+// have published (low half of the counter), polling with relaxed loads.
+// Bounded by the wall clock and, independently, by a count of polls (each
+// poll sleeps >= 128 cycles), so it ends even if the clock stood still.
+// Returns false when it gave up (or wait_ticks < 0: do not wait at all).
+__device__ __forceinline__ bool wait_for_producers(int* cnt, int ksplit, long long wait_ticks) {
+    if (wait_ticks < 0) return false;
+    if ((__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 0xFFFF) >= ksplit)
+        return true;
+    const long long t0 = wall_clock64();
+    for (int polls = 0;; ++polls) {
+        if ((__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 0xFFFF) >= ksplit)
+            return true;
+        if (wall_clock64() - t0 > wait_ticks || polls >= (1 << 22)) return false;
+        __builtin_amdgcn_s_sleep(2);
+    }
+}
+
+// Sum of the ksplit published chunk partials p[0], p[stride], ... in chunk
+// order, read with agent-scope loads (batches of 8 in flight).
+__device__ __forceinline__ float sum_partials_coherent(float* p, long long stride, int ksplit) {
+    float sum = 0.f;
+    for (int p0 = 0; p0 < ksplit; p0 += 8) {
+        float tv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            tv[u] = (p0 + u < ksplit) ? __hip_atomic_load(p + (long long)(p0 + u) * stride,
+                                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                      : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (p0 + u < ksplit) sum += tv[u];
+    }
+    return sum;
+}
+
+// Stores one partial sum so that it is visible at agent scope once the
+// storing wave's memory counter drains (write-through, no L2 write-back).
+__device__ __forceinline__ void store_partial(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Position of workgroup blockIdx.x among the items: shrink then expand items
+// of the first slots_a tile slots, then shrink then expand items of the
+// remaining slots_b.  Every expand item follows all shrink items of its tile.
+struct Item {
+    bool shrink;
+    int g;    // tile slot
+    int sub;  // H1 chunk (shrink) or column chunk (expand)
+};
+
+__device__ __forceinline__ Item decode_item(int slots_a, int slots_b, int ksplit, int csplit) {
+    long long item = blockIdx.x;
+    int base = 0, nslots = slots_a;
+    if (item >= (long long)slots_a * (ksplit + csplit)) {
+        item -= (long long)slots_a * (ksplit + csplit);
+        base = slots_a;
+        nslots = slots_b;
+    }
+    const long long n_shrink = (long long)nslots * ksplit;
+    Item it;
+    it.shrink = item < n_shrink;
+    if (it.shrink) {
+        it.g = base + (int)(item / ksplit);
+        it.sub = (int)(item % ksplit);
+    } else {
+        const long long e = item - n_shrink;
+        it.g = base + (int)(e / csplit);
+        it.sub = (int)(e % csplit);
+    }
+    return it;
+}
+
 template <typename DT, int R, int NT, int RB, int PG, int KB>
 __global__ __launch_bounds__(NT) void lora_fused_kernel(
     typename DT::storage* __restrict__ y, const typename DT::storage* __restrict__ x,
@@ -165,17 +238,7 @@ __global__ __launch_bounds__(NT) void lora_fused_kernel(
     const int tid = threadIdx.x;
     const long long row_stride = (long long)num_rows * R;  // between chunk partials
 
-    // Items in launch order: shrink then expand items of the slots_a first
-    // slots, then shrink then expand items of the slots_b remaining ones.
-    // Every expand item thus follows all shrink items of its tile.
-    long long item = blockIdx.x;
-    int base = 0, nslots = slots_a;
-    if (item >= (long long)slots_a * (ksplit + csplit)) {
-        item -= (long long)slots_a * (ksplit + csplit);
-        base = slots_a;
-        nslots = slots_b;
-    }
-    const long long n_shrink = (long long)nslots * ksplit;
+    const Item it = decode_item(slots_a, slots_b, ksplit, csplit);
     auto locate = [&](int g, Tile& t) {
         return compact ? locate_tile_compact<NT>(seg_indptr, adapter_ids, S, num_rows,
                                                  num_adapters, RB, g, s_scan, t)
@@ -183,10 +246,10 @@ __global__ __launch_bounds__(NT) void lora_fused_kernel(
                                          RB, g, s_scan, t);
     };
 
-    if (item < n_shrink) {
+    if (it.shrink) {
         // ---------------- shrink item ----------------
-        const int g = base + (int)(item / ksplit);
-        const int p = (int)(item % ksplit);
+        const int g = it.g;
+        const int p = it.sub;
         Tile tile;
         if (locate(g, tile)) {
             const int h_lo = p * h_per_split;
@@ -195,10 +258,8 @@ __global__ __launch_bounds__(NT) void lora_fused_kernel(
             const st* xr = x + (long long)tile.row0 * H1;
             float* out = partials + (long long)p * row_stride + (long long)tile.row0 * R;
             shrink_chunk<DT, R, NT, RB, PG>(
-                A, xr, tile.nrows, H1, h_lo, h_hi, s_red, [&](int i, int k, float v) {
-                    __hip_atomic_store(&out[i * R + k], v, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-                });
+                A, xr, tile.nrows, H1, h_lo, h_hi, s_red,
+                [&](int i, int k, float v) { store_partial(&out[i * R + k], v); });
             // Each wave waits for its partial stores to be acknowledged; the
             // barrier then lets thread 0 announce them.
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -208,9 +269,8 @@ __global__ __launch_bounds__(NT) void lora_fused_kernel(
         }
     } else {
         // ---------------- expand item ----------------
-        const long long e = item - n_shrink;
-        const int g = base + (int)(e / csplit);
-        const int c = (int)(e % csplit);
+        const int g = it.g;
+        const int c = it.sub;
         Tile tile;
         if (locate(g, tile)) {
             const int nrows = tile.nrows;
@@ -233,25 +293,7 @@ __global__ __launch_bounds__(NT) void lora_fused_kernel(
             if (tid == 0) {
                 // Poll with relaxed loads (no cache invalidation per poll);
                 // one acquire fence once the count is complete.
-                int ok = wait_ticks >= 0;  // negative: take the self-contained path
-                int* cnt = &counters[g * counter_stride];
-                if (ok && (__hip_atomic_load(cnt, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT) & 0xFFFF) < ksplit) {
-                    // Bounded by the wall clock and, independently, by a count
-                    // of polls (each poll sleeps >= 128 cycles), so the loop
-                    // ends even if the clock were to stand still.
-                    const long long t0 = wall_clock64();
-                    for (int polls = 0;; ++polls) {
-                        if ((__hip_atomic_load(cnt, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT) & 0xFFFF) >= ksplit)
-                            break;
-                        if (wall_clock64() - t0 > wait_ticks || polls >= (1 << 22)) {
-                            ok = 0;
-                            break;
-                        }
-                        __builtin_amdgcn_s_sleep(2);
-                    }
-                }
+                const int ok = wait_for_producers(&counters[g * counter_stride], ksplit, wait_ticks);
                 s_flag = ok;
             }
             __syncthreads();
@@ -262,23 +304,9 @@ __global__ __launch_bounds__(NT) void lora_fused_kernel(
                     const int i = t / R;
                     const int k = t - i * R;
                     float sum = 0.f;
-                    if (i < nrows) {
-                        float* vp = partials + (long long)(tile.row0 + i) * R + k;
-                        // Batches of loads in flight, summed in chunk order.
-                        for (int p0 = 0; p0 < ksplit; p0 += 8) {
-                            float tv[8];
-#pragma unroll
-                            for (int u = 0; u < 8; ++u)
-                                tv[u] = (p0 + u < ksplit)
-                                            ? __hip_atomic_load(vp + (long long)(p0 + u) * row_stride,
-                                                                __ATOMIC_RELAXED,
-                                                                __HIP_MEMORY_SCOPE_AGENT)
-                                            : 0.f;
-#pragma unroll
-                            for (int u = 0; u < 8; ++u)
-                                if (p0 + u < ksplit) sum += tv[u];
-                        }
-                    }
+                    if (i < nrows)
+                        sum = sum_partials_coherent(partials + (long long)(tile.row0 + i) * R + k,
+                                                    row_stride, ksplit);
                     s_v[t] = sum;
                 }
             } else {

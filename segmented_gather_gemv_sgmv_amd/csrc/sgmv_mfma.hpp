@@ -1,0 +1,330 @@
+// sgmv_mfma.hpp -- lora_apply for segments of many rows (prefill shapes):
+// 16-row tiles whose two contractions run on the gfx950 matrix cores.
+//
+// Per tile of up to 16 rows of one segment (adapter a), the shrink
+// V = X A_a  ([16 x H1] x [H1 x r]) and the expand Y += s V B_a
+// ([16 x r] x [r x H2]) are dense contractions once several rows share an
+// adapter, so they use v_mfma_f32_16x16x32_{f16,bf16} with float32
+// accumulation (the two SGMV steps of Punica walkthrough,
+// omica.com.cn/news/959180, section 2.2).  The work is still bound by HBM
+// (x is read once and y read and written once), so the kernel keeps the
+// single-launch hand-off of sgmv_fused.hpp: shrink items (tile, H1 chunk)
+// publish float32 chunk partials, expand items (tile, column chunk) wait for
+// them, and the per-tile counters reset themselves.
+//
+// Operand layouts of the 16x16x32 MFMA (checked on the device): lane l holds
+// A[l % 16][8 (l / 16) + j] and B[8 (l / 16) + j][l % 16], j = 0..7, and
+// receives D[4 (l / 16) + i][l % 16], i = 0..3.
+//
+// Shrink: X is the A operand, loaded straight from global memory (8
+// consecutive h of one row = 16 bytes).  A_a is stored [h][r] (r fastest),
+// so the B operand (8 consecutive h of one column) is gathered from an LDS
+// copy of the chunk.  The four waves split the chunk's h range and their
+// 16 x r results are summed in LDS in a fixed order.
+//
+// Expand: computed as Y^T = B^T V^T so that each lane's result is 4
+// consecutive columns of one row (one 8-byte y access).  B^T is gathered
+// from an LDS copy of the B chunk.  V is float32; to feed it to a 16-bit
+// MFMA without losing precision it is split as v = hi + lo (both 16-bit)
+// and the K dimension is [hi | lo] against [B ; B], which keeps about 22
+// (fp16) or 16 (bf16) significant bits of v.  For fp16 the tile's v is first
+// scaled by a power of two so that max |v| lies in [2^12, 2^13) (exact,
+// undone on the result), keeping hi inside the fp16 range.
+#pragma once
+
+#include "sgmv_device.hpp"
+#include "sgmv_fused.hpp"
+
+namespace sgmv {
+
+typedef float mf32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 mf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 mbf16x8 __attribute__((ext_vector_type(8)));
+
+template <typename DT>
+struct MfmaOps;
+
+template <>
+struct MfmaOps<F16> {
+    static constexpr bool kScaleV = true;  // keep v inside the fp16 range
+    __device__ static __forceinline__ mf32x4 mma(const uint4& a, const uint4& b, mf32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(mf16x8, a),
+                                                      __builtin_bit_cast(mf16x8, b), c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ uint32_t bits(float f) { return F16::f2h(f); }
+    __device__ static __forceinline__ float value(uint32_t b) { return F16::h2f(b); }
+};
+
+template <>
+struct MfmaOps<BF16> {
+    static constexpr bool kScaleV = false;  // bf16 has float32's exponent range
+    __device__ static __forceinline__ mf32x4 mma(const uint4& a, const uint4& b, mf32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mbf16x8, a),
+                                                       __builtin_bit_cast(mbf16x8, b), c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ uint32_t bits(float f) { return BF16::f2b(f); }
+    __device__ static __forceinline__ float value(uint32_t b) { return BF16::b2f(b); }
+};
+
+__device__ __forceinline__ uint2 load8(const void* p) { return *reinterpret_cast<const uint2*>(p); }
+__device__ __forceinline__ void store8(void* p, const uint2& v) { *reinterpret_cast<uint2*>(p) = v; }
+
+// Packs eight 16-bit values into the 16 bytes of an MFMA operand.
+__device__ __forceinline__ uint4 pack8(const uint32_t (&h)[8]) {
+    return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                      h[6] | (h[7] << 16));
+}
+
+template <int R>
+struct MfmaShape {
+    static constexpr int kT = 16;                        // rows per tile
+    static constexpr int kNT = 256;                      // threads per workgroup
+    static constexpr int kNW = kNT / kWave;              // waves
+    static constexpr int kKcMax = 16384 / R;             // rows of A per chunk (32 KB of LDS)
+    static constexpr int kXSteps = kKcMax / (32 * kNW);  // K steps of 32 per wave and chunk
+    static constexpr int kCW = (8192 / R) < 512 ? (8192 / R) : 512;  // expand columns per item
+    static constexpr int kCBW = kCW / (16 * kNW);        // 16-column blocks per wave
+    static_assert(R % 16 == 0 && R <= 128, "MFMA path needs r in {16, 32, 64, 128}");
+};
+
+// One H1 chunk [h_lo, h_hi) of the shrink for a tile of nrows <= 16 rows,
+// reduced across the workgroup; calls emit(i, k, value) once per (i < nrows,
+// k < R) from threads tid < 16 * R.  h_lo and h_hi are multiples of 8 and
+// h_hi - h_lo <= kKcMax.  Begins and ends with the block synchronised.
+template <typename DT, int R, typename Emit>
+__device__ __forceinline__ void shrink_chunk_mfma(const typename DT::storage* __restrict__ A,
+                                                  const typename DT::storage* __restrict__ xr,
+                                                  int nrows, int H1, int h_lo, int h_hi,
+                                                  uint16_t* s_a, float* s_red, Emit&& emit) {
+    using Sh = MfmaShape<R>;
+    using Ops = MfmaOps<DT>;
+    constexpr int NB = R / 16;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wid = tid / kWave;
+    const int m = lane & 15;   // operand row (A) / column (B) of this lane
+    const int grp = lane >> 4; // which 8 of the 32 K values
+    const int kc = h_hi - h_lo;
+    const int kq = (kc + 32 * Sh::kNW - 1) / (32 * Sh::kNW) * 32;  // h rows per wave
+
+    // x operand for all of this wave's K steps, issued before anything waits.
+    uint4 xa[Sh::kXSteps];
+#pragma unroll
+    for (int s = 0; s < Sh::kXSteps; ++s) {
+        const int hl = wid * kq + s * 32 + grp * 8;
+        xa[s] = (s * 32 < kq && hl < kc && m < nrows)
+                    ? load16(xr + (long long)m * H1 + h_lo + hl)
+                    : make_uint4(0, 0, 0, 0);
+    }
+    // The chunk of A, as stored ([h][r]), into LDS.
+    const typename DT::storage* Ac = A + (long long)h_lo * R;
+    for (int t = tid; t < kc * R / 8; t += Sh::kNT)
+        store16(s_a + t * 8, load16(Ac + (long long)t * 8));
+    __syncthreads();
+
+    mf32x4 acc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = mf32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < Sh::kXSteps; ++s) {
+        const int hl = wid * kq + s * 32 + grp * 8;
+        if (s * 32 < kq) {  // wave-uniform
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                uint32_t hb[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    hb[j] = hl < kc ? (uint32_t)s_a[(hl + j) * R + nb * 16 + m] : 0u;
+                acc[nb] = Ops::mma(xa[s], pack8(hb), acc[nb]);
+            }
+        }
+    }
+    // Cross-wave sum in a fixed order.
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s_red[(wid * 16 + 4 * grp + i) * R + nb * 16 + m] = acc[nb][i];
+    __syncthreads();
+    for (int t = tid; t < 16 * R; t += Sh::kNT) {
+        const int i = t / R;
+        const int k = t - i * R;
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < Sh::kNW; ++w) sum += s_red[(w * 16 + i) * R + k];
+        if (i < nrows) emit(i, k, sum);
+    }
+    __syncthreads();  // s_a and s_red free again
+}
+
+template <typename DT, int R>
+__global__ __launch_bounds__(256) void lora_mfma_kernel(
+    typename DT::storage* __restrict__ y, const typename DT::storage* __restrict__ x,
+    const typename DT::storage* __restrict__ A_stack,
+    const typename DT::storage* __restrict__ B_stack, const int* __restrict__ seg_indptr,
+    const int* __restrict__ adapter_ids, int S, int num_rows, int num_adapters, int H1, int H2,
+    float scale, float* __restrict__ partials, int* __restrict__ counters, int ksplit,
+    int h_per_split, int csplit, int slots_a, int slots_b, int compact, int n_counters,
+    int counter_stride, long long wait_ticks) {
+    using st = typename DT::storage;
+    using Sh = MfmaShape<R>;
+    using Ops = MfmaOps<DT>;
+    constexpr int T = Sh::kT;
+    constexpr int NT = Sh::kNT;
+    constexpr int NW = Sh::kNW;
+    constexpr int CW = Sh::kCW;
+    constexpr int CBW = Sh::kCBW;
+    constexpr int BV = R * CW / 8 / NT;  // 16-byte vectors of the B chunk per thread
+    static_assert(R * CW / 8 == BV * NT, "B chunk must split evenly over the threads");
+
+    __shared__ int s_scan[NW + 4];
+    __shared__ __align__(16) uint16_t s_a[Sh::kKcMax * R];  // A chunk; later the B chunk [R][CW]
+    __shared__ float s_red[NW * 16 * R];
+    __shared__ float s_v[T * R];
+    __shared__ __align__(16) uint16_t s_vh[T * 2 * R];      // per row: hi[0..R), lo[0..R)
+    __shared__ float s_max[NW];
+    __shared__ int s_flag;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wid = tid / kWave;
+    const long long row_stride = (long long)num_rows * R;
+    const int total = ksplit + (csplit << 16);
+    const Item it = decode_item(slots_a, slots_b, ksplit, csplit);
+    Tile tile;
+    const bool have =
+        compact ? locate_tile_compact<NT>(seg_indptr, adapter_ids, S, num_rows, num_adapters, T,
+                                          it.g, s_scan, tile)
+                : locate_tile<NT>(seg_indptr, adapter_ids, S, num_rows, num_adapters, T, it.g,
+                                  s_scan, tile);
+    if (!have) return;
+    const int nrows = tile.nrows;
+    const st* A = A_stack + (long long)tile.adapter * H1 * R;
+    const st* xr = x + (long long)tile.row0 * H1;
+    int* cnt = &counters[it.g * counter_stride];
+
+    if (it.shrink) {
+        const int h_lo = it.sub * h_per_split;
+        const int h_hi = min(H1, h_lo + h_per_split);
+        float* out = partials + (long long)it.sub * row_stride + (long long)tile.row0 * R;
+        shrink_chunk_mfma<DT, R>(A, xr, nrows, H1, h_lo, h_hi, s_a, s_red,
+                                 [&](int i, int k, float v) { store_partial(&out[i * R + k], v); });
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are acknowledged
+        __syncthreads();
+        if (tid == 0) depart(cnt, 1, total);
+        return;
+    }
+
+    // ---------------- expand item ----------------
+    const int c0 = it.sub * CW;
+    const st* Bc = B_stack + (long long)tile.adapter * R * H2 + c0;
+    const int m = lane & 15;
+    const int grp = lane >> 4;
+    // Loads that do not depend on v: the B chunk and this lane's y values.
+    uint4 bq[BV];
+#pragma unroll
+    for (int u = 0; u < BV; ++u) {
+        const int t = tid + u * NT;
+        const int kr = t / (CW / 8);
+        const int c8 = (t % (CW / 8)) * 8;
+        bq[u] = (c0 + c8 < H2) ? load16(Bc + (long long)kr * H2 + c8) : make_uint4(0, 0, 0, 0);
+    }
+    uint2 yq[CBW];
+#pragma unroll
+    for (int q = 0; q < CBW; ++q) {
+        const int col = c0 + (wid * CBW + q) * 16 + 4 * grp;
+        yq[q] = (m < nrows && col < H2) ? load8(y + (long long)(tile.row0 + m) * H2 + col)
+                                        : make_uint2(0, 0);
+    }
+    if (tid == 0) s_flag = wait_for_producers(cnt, ksplit, wait_ticks);
+    __syncthreads();
+    if (s_flag) {
+        for (int t = tid; t < T * R; t += NT) {
+            const int i = t / R;
+            const int k = t - i * R;
+            s_v[t] = i < nrows ? sum_partials_coherent(
+                                     partials + (long long)(tile.row0 + i) * R + k, row_stride,
+                                     ksplit)
+                               : 0.f;
+        }
+    } else {
+        // The producers are late: compute every chunk here, summing in the
+        // same order as the normal path.
+        if (tid == 0)
+            __hip_atomic_store(&counters[n_counters - 1], 1, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        for (int t = tid; t < T * R; t += NT) s_v[t] = 0.f;
+        __syncthreads();
+        for (int pp = 0; pp < ksplit; ++pp) {
+            const int h_lo = pp * h_per_split;
+            const int h_hi = min(H1, h_lo + h_per_split);
+            shrink_chunk_mfma<DT, R>(A, xr, nrows, H1, h_lo, h_hi, s_a, s_red,
+                                     [&](int i, int k, float v) { s_v[i * R + k] += v; });
+        }
+    }
+    __syncthreads();
+    if (tid == 0) depart(cnt, 1 << 16, total);
+
+    // B chunk into LDS; the largest |v| of the tile for the fp16 range scaling.
+    uint16_t* s_b = s_a;
+#pragma unroll
+    for (int u = 0; u < BV; ++u) {
+        const int t = tid + u * NT;
+        store16(s_b + (t / (CW / 8)) * CW + (t % (CW / 8)) * 8, bq[u]);
+    }
+    int shift = 0;
+    if constexpr (Ops::kScaleV) {
+        float mx = 0.f;
+        for (int t = tid; t < T * R; t += NT) mx = fmaxf(mx, fabsf(s_v[t]));
+#pragma unroll
+        for (int d = 32; d > 0; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d));
+        if (lane == 0) s_max[wid] = mx;
+        __syncthreads();
+        mx = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+        if (mx > 0.f && mx <= 3.0e38f) {
+            int e;
+            frexpf(mx, &e);  // mx = f * 2^e, f in [0.5, 1)
+            shift = min(max(13 - e, -100), 100);
+        }
+    }
+    for (int t = tid; t < T * R; t += NT) {
+        const int i = t / R;
+        const int k = t - i * R;
+        const float v = ldexpf(s_v[t], shift);
+        const uint32_t hi = Ops::bits(v);
+        const uint32_t lo = Ops::bits(v - Ops::value(hi));
+        s_vh[i * 2 * R + k] = (uint16_t)hi;
+        s_vh[i * 2 * R + R + k] = (uint16_t)lo;
+    }
+    __syncthreads();
+
+    const float out_scale = ldexpf(scale, -shift);
+#pragma unroll
+    for (int q = 0; q < CBW; ++q) {
+        const int cb = wid * CBW + q;
+        mf32x4 acc = mf32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2 * R / 32; ++ks) {
+            uint32_t ab[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int kr = (ks * 32 + grp * 8 + j) % R;  // hi and lo both meet B row kr
+                ab[j] = s_b[kr * CW + cb * 16 + m];
+            }
+            const uint4 bv = *reinterpret_cast<const uint4*>(s_vh + m * 2 * R + ks * 32 + grp * 8);
+            acc = Ops::mma(pack8(ab), bv, acc);
+        }
+        const int col = c0 + cb * 16 + 4 * grp;
+        if (m < nrows && col < H2) {
+            float yf[4];
+            DT::unpack2(yq[q].x, yf);
+            DT::unpack2(yq[q].y, yf + 2);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) yf[i] = fmaf(out_scale, acc[i], yf[i]);
+            store8(y + (long long)(tile.row0 + m) * H2 + col,
+                   make_uint2(DT::pack2(yf[0], yf[1]), DT::pack2(yf[2], yf[3])));
+        }
+    }
+}
+
+}  // namespace sgmv
