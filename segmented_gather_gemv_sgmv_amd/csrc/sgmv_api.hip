@@ -200,6 +200,42 @@ MfmaPlan make_mfma_plan(int num_rows, int num_segments, int H1, int H2, int r, i
     return f;
 }
 
+// Plan of the two-launch MFMA form (shrink_mfma_kernel, then
+// expand_mfma_kernel), taken when the single-kernel form would need more
+// than two rounds of resident items: then waiting items hold slots that
+// streaming ones could use, and one more launch costs little.
+struct MfmaSplitPlan {
+    bool ok;
+    int compact;
+    long long slots;
+    int ksplit, h_per_split, csplit;
+    long long grid_shrink, grid_expand;
+};
+
+MfmaSplitPlan make_mfma_split_plan(const MfmaPlan& mp, int H1, int H2, int r) {
+    MfmaSplitPlan sp{};
+    if (!mp.ok) return sp;
+    sp.compact = mp.compact;
+    sp.slots = mp.slots_a + mp.slots_b;
+    if (sp.slots * (mp.ksplit + mp.csplit) <= 2LL * kFusedItems) return sp;
+    const int kc_max = 16384 / r;
+    const int cw = (8192 / r) < 512 ? (8192 / r) : 512;
+    sp.csplit = (H2 + cw - 1) / cw;
+    // Fewest chunks that fit the LDS copy of A, more while the shrink launch
+    // has fewer than kTargetWorkgroups workgroups and chunks keep >= 256 rows.
+    long long k = (H1 + kc_max - 1) / kc_max;
+    while (sp.slots * k < kTargetWorkgroups && H1 / (k * 2) >= 256) k *= 2;
+    long long hps = (H1 + k - 1) / k;
+    hps = (hps + 127) / 128 * 128;
+    if (hps > kc_max) hps = kc_max;
+    sp.h_per_split = (int)hps;
+    sp.ksplit = (int)((H1 + hps - 1) / hps);
+    sp.grid_shrink = sp.slots * sp.ksplit;
+    sp.grid_expand = sp.slots * sp.csplit;
+    sp.ok = sp.grid_shrink <= kMaxGrid && sp.grid_expand <= kMaxGrid;
+    return sp;
+}
+
 bool use_mfma(int num_rows, int num_segments) {
     return (long long)num_rows >= (long long)kMfmaRowsPerSegment * num_segments;
 }
@@ -438,6 +474,8 @@ size_t lora_apply_workspace_bytes(int32_t num_rows, int32_t num_segments, int32_
     int k = p.ksplit;
     if (f.ok && f.ksplit > k) k = f.ksplit;
     if (mp.ok && mp.ksplit > k) k = mp.ksplit;
+    const MfmaSplitPlan sp = make_mfma_split_plan(mp, H1, H2, r);
+    if (sp.ok && sp.ksplit > k) k = sp.ksplit;
     return kCounterBytes + (size_t)k * (size_t)num_rows * (size_t)r * sizeof(float);
 }
 
@@ -519,10 +557,22 @@ int lora_apply(void* y, const void* x, const void* A_stack, const void* B_stack,
         wait_s < 1e-300 ? -1 : (long long)(wait_s * (double)wall_ticks_per_second());
     const MfmaPlan mp = make_mfma_plan(num_rows, num_segments, H1, H2, r, dtype);
     if (mp.ok && aligned && aligned16(x) && use_mfma(num_rows, num_segments)) {
+        const MfmaSplitPlan sp = make_mfma_split_plan(mp, H1, H2, r);
         auto go = [&](auto dt, auto rank) {
             using DT = decltype(dt);
             using T = typename DT::storage;
             constexpr int R = decltype(rank)::value;
+            if (sp.ok) {
+                launch(&shrink_mfma_kernel<DT, R>, dim3((unsigned)sp.grid_shrink), dim3(256), st,
+                       (const T*)x, (const T*)A_stack, seg_indptr, adapter_ids, num_segments,
+                       num_rows, num_adapters, H1, part, sp.ksplit, sp.h_per_split, sp.compact);
+                if (t_pending != hipSuccess) return;  // no expand over partials never written
+                launch(&expand_mfma_kernel<DT, R>, dim3((unsigned)sp.grid_expand), dim3(256), st,
+                       (T*)y, (const T*)B_stack, seg_indptr, adapter_ids, num_segments, num_rows,
+                       num_adapters, H2, scale, (const float*)part, sp.ksplit, sp.csplit,
+                       sp.compact);
+                return;
+            }
             launch(&lora_mfma_kernel<DT, R>, dim3((unsigned)mp.grid), dim3(256), st, (T*)y,
                    (const T*)x, (const T*)A_stack, (const T*)B_stack, seg_indptr, adapter_ids,
                    num_segments, num_rows, num_adapters, H1, H2, scale, part, counters,

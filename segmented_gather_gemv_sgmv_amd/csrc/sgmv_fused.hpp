@@ -140,6 +140,19 @@ __device__ __forceinline__ void depart(int* counter, int amount, int total) {
         __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// An expand item counts itself out in two steps so that the round trip of
+// its atomic overlaps its compute: depart_begin() issues the addition once
+// the partials are in LDS (nothing it does afterwards touches the partials
+// or the counter, so nothing needs to complete first), and depart_end(),
+// after the compute, resets the counter if this item completed the count.
+__device__ __forceinline__ int depart_begin(int* counter, int amount) {
+    return __hip_atomic_fetch_add(counter, amount, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void depart_end(int* counter, int before, int amount, int total) {
+    if (before + amount == total)
+        __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Thread 0 of an expand item: waits until the tile's ksplit shrink items
 // have published (low half of the counter), polling with relaxed loads.
 // Bounded by the wall clock and, independently, by a count of polls (each
@@ -338,7 +351,8 @@ __global__ __launch_bounds__(NT) void lora_fused_kernel(
             }
             __syncthreads();
             // The partials are in LDS now: this item no longer needs them.
-            if (tid == 0) depart(&counters[g * counter_stride], 1 << 16, ksplit + (csplit << 16));
+            int before = 0;
+            if (tid == 0) before = depart_begin(&counters[g * counter_stride], 1 << 16);
 
             float acc[RB][VEC];
 #pragma unroll
@@ -379,6 +393,8 @@ __global__ __launch_bounds__(NT) void lora_fused_kernel(
                     }
                 }
             }
+            if (tid == 0)
+                depart_end(&counters[g * counter_stride], before, 1 << 16, ksplit + (csplit << 16));
         }
     }
 

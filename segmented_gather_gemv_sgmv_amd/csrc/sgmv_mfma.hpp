@@ -84,6 +84,17 @@ struct MfmaShape {
     static constexpr int kXSteps = kKcMax / (32 * kNW);  // K steps of 32 per wave and chunk
     static constexpr int kCW = (8192 / R) < 512 ? (8192 / R) : 512;  // expand columns per item
     static constexpr int kCBW = kCW / (16 * kNW);        // 16-column blocks per wave
+    static constexpr int kBV = R * kCW / 8 / kNT;        // 16-byte B vectors per thread
+    // Epilogue: the tile's results (16 x kCW floats) go through LDS so that y
+    // is read and written in row-contiguous 16-byte pieces: kYU pieces of 8
+    // columns per thread (a wave covers 512 columns).  In LDS, float4 f of
+    // row i sits at position f ^ (i & 15), so that neither the MFMA-layout
+    // writes nor the row reads meet bank conflicts.
+    static constexpr int kYU = (2 * kCW + kNT - 1) / kNT;
+    // LDS (in 16-bit units) of the B chunk, reused for the results
+    static constexpr int kStageB = R * kCW > 2 * kT * kCW ? R * kCW : 2 * kT * kCW;
+    static_assert(kCW % 64 == 0, "the swizzle needs at least 16 float4 per row");
+    static_assert(kBV * kNT * 8 == R * kCW, "B chunk must split evenly over the threads");
     static_assert(R % 16 == 0 && R <= 128, "MFMA path needs r in {16, 32, 64, 128}");
 };
 
@@ -116,10 +127,22 @@ __device__ __forceinline__ void shrink_chunk_mfma(const typename DT::storage* __
                     ? load16(xr + (long long)m * H1 + h_lo + hl)
                     : make_uint4(0, 0, 0, 0);
     }
-    // The chunk of A, as stored ([h][r]), into LDS.
+    // The chunk of A, as stored ([h][r]), into LDS: every load in flight
+    // before the first LDS store.
     const typename DT::storage* Ac = A + (long long)h_lo * R;
-    for (int t = tid; t < kc * R / 8; t += Sh::kNT)
-        store16(s_a + t * 8, load16(Ac + (long long)t * 8));
+    constexpr int kAV = Sh::kKcMax * R / 8 / Sh::kNT;  // 16-byte pieces per thread
+    static_assert(kAV * Sh::kNT * 8 == Sh::kKcMax * R, "A chunk must split evenly");
+    uint4 av[kAV];
+#pragma unroll
+    for (int u = 0; u < kAV; ++u) {
+        const int t = tid + u * Sh::kNT;
+        av[u] = t < kc * R / 8 ? load16(Ac + (long long)t * 8) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kAV; ++u) {
+        const int t = tid + u * Sh::kNT;
+        if (t < kc * R / 8) store16(s_a + t * 8, av[u]);
+    }
     __syncthreads();
 
     mf32x4 acc[NB];
@@ -156,6 +179,146 @@ __device__ __forceinline__ void shrink_chunk_mfma(const typename DT::storage* __
     __syncthreads();  // s_a and s_red free again
 }
 
+// The part of an expand item (tile rows x columns [c0, c0 + kCW)) that does
+// not depend on v, loaded first: this thread's 16-byte pieces of the B chunk
+// and the y values its lane updates.
+template <int R>
+struct ExpandRegs {
+    uint4 bq[MfmaShape<R>::kBV];
+    uint4 yv[MfmaShape<R>::kYU];  // piece u: row u / (kCW / 8), columns 8 (u % (kCW / 8)) + [0, 8)
+};
+
+template <typename DT, int R>
+__device__ __forceinline__ void expand_prefetch(ExpandRegs<R>& e,
+                                                const typename DT::storage* __restrict__ B,
+                                                const typename DT::storage* __restrict__ yr,
+                                                int nrows, int H2, int c0) {
+    using Sh = MfmaShape<R>;
+    constexpr int CW = Sh::kCW;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < Sh::kBV; ++u) {
+        const int t = tid + u * Sh::kNT;
+        const int kr = t / (CW / 8);
+        const int c8 = (t % (CW / 8)) * 8;
+        e.bq[u] = (c0 + c8 < H2) ? load16(B + (long long)kr * H2 + c0 + c8)
+                                 : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < Sh::kYU; ++j) {
+        const int u = tid + j * Sh::kNT;
+        const int row = u / (CW / 8);
+        const int col = c0 + (u % (CW / 8)) * 8;
+        e.yv[j] = (u < 2 * CW && row < nrows && col < H2)
+                      ? load16(yr + (long long)row * H2 + col)
+                      : make_uint4(0, 0, 0, 0);
+    }
+}
+
+// Finishes an expand item once s_v (16 x R floats, rows >= nrows zero) is
+// complete and visible to the block: y[rows, c0 : c0 + kCW] += scale * V B.
+// The B chunk goes to LDS (s_b, kStageB 16-bit units), v is split into
+// 16-bit hi/lo halves (s_vh, range-scaled for fp16), Y^T = B^T V^T runs on
+// the MFMA units, and the results return through s_b so that y moves in
+// row-contiguous pieces.
+template <typename DT, int R>
+__device__ __forceinline__ void expand_apply(const ExpandRegs<R>& e, uint16_t* s_b,
+                                             const float* s_v, uint16_t* s_vh, float* s_max,
+                                             typename DT::storage* __restrict__ yr, int nrows,
+                                             int H2, int c0, float scale) {
+    using Sh = MfmaShape<R>;
+    using Ops = MfmaOps<DT>;
+    constexpr int T = Sh::kT;
+    constexpr int NT = Sh::kNT;
+    constexpr int CW = Sh::kCW;
+    constexpr int CBW = Sh::kCBW;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wid = tid / kWave;
+    const int m = lane & 15;
+    const int grp = lane >> 4;
+#pragma unroll
+    for (int u = 0; u < Sh::kBV; ++u) {
+        const int t = tid + u * NT;
+        store16(s_b + (t / (CW / 8)) * CW + (t % (CW / 8)) * 8, e.bq[u]);
+    }
+    // The largest |v| of the tile for the fp16 range scaling.
+    int shift = 0;
+    if constexpr (Ops::kScaleV) {
+        float mx = 0.f;
+        for (int t = tid; t < T * R; t += NT) mx = fmaxf(mx, fabsf(s_v[t]));
+#pragma unroll
+        for (int d = 32; d > 0; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d));
+        if (lane == 0) s_max[wid] = mx;
+        __syncthreads();
+        mx = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+        if (mx > 0.f && mx <= 3.0e38f) {
+            int ex;
+            frexpf(mx, &ex);  // mx = f * 2^ex, f in [0.5, 1)
+            shift = min(max(13 - ex, -100), 100);
+        }
+    }
+    for (int t = tid; t < T * R; t += NT) {
+        const int i = t / R;
+        const int k = t - i * R;
+        const float v = ldexpf(s_v[t], shift);
+        const uint32_t hi = Ops::bits(v);
+        const uint32_t lo = Ops::bits(v - Ops::value(hi));
+        s_vh[i * 2 * R + k] = (uint16_t)hi;
+        s_vh[i * 2 * R + R + k] = (uint16_t)lo;
+    }
+    __syncthreads();
+
+    const float out_scale = ldexpf(scale, -shift);
+    mf32x4 acc[CBW];
+#pragma unroll
+    for (int q = 0; q < CBW; ++q) {
+        const int cb = wid * CBW + q;
+        acc[q] = mf32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2 * R / 32; ++ks) {
+            uint32_t ab[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int kr = (ks * 32 + grp * 8 + j) % R;  // hi and lo both meet B row kr
+                ab[j] = s_b[kr * CW + cb * 16 + m];
+            }
+            const uint4 bv = *reinterpret_cast<const uint4*>(s_vh + m * 2 * R + ks * 32 + grp * 8);
+            acc[q] = Ops::mma(pack8(ab), bv, acc[q]);
+        }
+    }
+    // Results to LDS over the B chunk (every wave is done with it), lane
+    // (m, grp) holding columns cb * 16 + 4 grp + [0, 4) of row m.
+    __syncthreads();
+    float* s_y = reinterpret_cast<float*>(s_b);
+#pragma unroll
+    for (int q = 0; q < CBW; ++q) {
+        const int f = (wid * CBW + q) * 4 + grp;  // float4 index of columns cb * 16 + 4 grp
+        *reinterpret_cast<float4*>(s_y + m * CW + ((f ^ m) << 2)) =
+            make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
+    }
+    __syncthreads();
+    // y += scale * result, 8 columns of one row per piece.
+#pragma unroll
+    for (int j = 0; j < Sh::kYU; ++j) {
+        const int u = tid + j * NT;
+        const int row = u / (CW / 8);
+        const int cl = (u % (CW / 8)) * 8;
+        if (u < 2 * CW && row < nrows && c0 + cl < H2) {
+            const int f = cl >> 2;
+            const float4 r0 = *reinterpret_cast<const float4*>(s_y + row * CW + ((f ^ row) << 2));
+            const float4 r1 =
+                *reinterpret_cast<const float4*>(s_y + row * CW + (((f + 1) ^ row) << 2));
+            const float rv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+            float yf[8];
+            DT::unpack(e.yv[j], yf);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) yf[i] = fmaf(out_scale, rv[i], yf[i]);
+            store16(yr + (long long)row * H2 + c0 + cl, DT::pack(yf));
+        }
+    }
+}
+
 template <typename DT, int R>
 __global__ __launch_bounds__(256) void lora_mfma_kernel(
     typename DT::storage* __restrict__ y, const typename DT::storage* __restrict__ x,
@@ -167,17 +330,15 @@ __global__ __launch_bounds__(256) void lora_mfma_kernel(
     int counter_stride, long long wait_ticks) {
     using st = typename DT::storage;
     using Sh = MfmaShape<R>;
-    using Ops = MfmaOps<DT>;
     constexpr int T = Sh::kT;
     constexpr int NT = Sh::kNT;
     constexpr int NW = Sh::kNW;
     constexpr int CW = Sh::kCW;
-    constexpr int CBW = Sh::kCBW;
-    constexpr int BV = R * CW / 8 / NT;  // 16-byte vectors of the B chunk per thread
-    static_assert(R * CW / 8 == BV * NT, "B chunk must split evenly over the threads");
 
     __shared__ int s_scan[NW + 4];
-    __shared__ __align__(16) uint16_t s_a[Sh::kKcMax * R];  // A chunk; later the B chunk [R][CW]
+    // A chunk; later the B chunk [R][CW] and then the expand results
+    __shared__ __align__(16) uint16_t s_a[Sh::kKcMax * R > Sh::kStageB ? Sh::kKcMax * R
+                                                                       : Sh::kStageB];
     __shared__ float s_red[NW * 16 * R];
     __shared__ float s_v[T * R];
     __shared__ __align__(16) uint16_t s_vh[T * 2 * R];      // per row: hi[0..R), lo[0..R)
@@ -185,8 +346,6 @@ __global__ __launch_bounds__(256) void lora_mfma_kernel(
     __shared__ int s_flag;
 
     const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wid = tid / kWave;
     const long long row_stride = (long long)num_rows * R;
     const int total = ksplit + (csplit << 16);
     const Item it = decode_item(slots_a, slots_b, ksplit, csplit);
@@ -217,25 +376,9 @@ __global__ __launch_bounds__(256) void lora_mfma_kernel(
 
     // ---------------- expand item ----------------
     const int c0 = it.sub * CW;
-    const st* Bc = B_stack + (long long)tile.adapter * R * H2 + c0;
-    const int m = lane & 15;
-    const int grp = lane >> 4;
-    // Loads that do not depend on v: the B chunk and this lane's y values.
-    uint4 bq[BV];
-#pragma unroll
-    for (int u = 0; u < BV; ++u) {
-        const int t = tid + u * NT;
-        const int kr = t / (CW / 8);
-        const int c8 = (t % (CW / 8)) * 8;
-        bq[u] = (c0 + c8 < H2) ? load16(Bc + (long long)kr * H2 + c8) : make_uint4(0, 0, 0, 0);
-    }
-    uint2 yq[CBW];
-#pragma unroll
-    for (int q = 0; q < CBW; ++q) {
-        const int col = c0 + (wid * CBW + q) * 16 + 4 * grp;
-        yq[q] = (m < nrows && col < H2) ? load8(y + (long long)(tile.row0 + m) * H2 + col)
-                                        : make_uint2(0, 0);
-    }
+    ExpandRegs<R> er;
+    expand_prefetch<DT, R>(er, B_stack + (long long)tile.adapter * R * H2,
+                           y + (long long)tile.row0 * H2, nrows, H2, c0);
     if (tid == 0) s_flag = wait_for_producers(cnt, ksplit, wait_ticks);
     __syncthreads();
     if (s_flag) {
@@ -261,70 +404,101 @@ __global__ __launch_bounds__(256) void lora_mfma_kernel(
             shrink_chunk_mfma<DT, R>(A, xr, nrows, H1, h_lo, h_hi, s_a, s_red,
                                      [&](int i, int k, float v) { s_v[i * R + k] += v; });
         }
+        // Load B and y again, so that the prefetched registers are not held
+        // across this rarely taken path.
+        expand_prefetch<DT, R>(er, B_stack + (long long)tile.adapter * R * H2,
+                               y + (long long)tile.row0 * H2, nrows, H2, c0);
     }
     __syncthreads();
-    if (tid == 0) depart(cnt, 1 << 16, total);
+    // The partials are in LDS now: count out, and reset after the compute.
+    int before = 0;
+    if (tid == 0) before = depart_begin(cnt, 1 << 16);
+    expand_apply<DT, R>(er, s_a, s_v, s_vh, s_max, y + (long long)tile.row0 * H2, nrows, H2, c0,
+                        scale);
+    if (tid == 0) depart_end(cnt, before, 1 << 16, total);
+}
 
-    // B chunk into LDS; the largest |v| of the tile for the fp16 range scaling.
-    uint16_t* s_b = s_a;
-#pragma unroll
-    for (int u = 0; u < BV; ++u) {
-        const int t = tid + u * NT;
-        store16(s_b + (t / (CW / 8)) * CW + (t % (CW / 8)) * 8, bq[u]);
-    }
-    int shift = 0;
-    if constexpr (Ops::kScaleV) {
-        float mx = 0.f;
-        for (int t = tid; t < T * R; t += NT) mx = fmaxf(mx, fabsf(s_v[t]));
-#pragma unroll
-        for (int d = 32; d > 0; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d));
-        if (lane == 0) s_max[wid] = mx;
-        __syncthreads();
-        mx = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
-        if (mx > 0.f && mx <= 3.0e38f) {
-            int e;
-            frexpf(mx, &e);  // mx = f * 2^e, f in [0.5, 1)
-            shift = min(max(13 - e, -100), 100);
-        }
-    }
-    for (int t = tid; t < T * R; t += NT) {
+// ---------------------------------------------------------------------------
+// The same computation as two launches, for calls large enough that the
+// second launch costs little next to the data: every shrink workgroup (tile,
+// H1 chunk) stores its float32 chunk partials, and after the launch boundary
+// every expand workgroup (tile, column chunk) sums them in chunk order and
+// applies them.  No workgroup waits on another, so each streams its data
+// with the whole chip busy, instead of holding a slot while it waits.  The
+// arithmetic and its order are those of lora_mfma_kernel.
+// ---------------------------------------------------------------------------
+template <typename DT, int R>
+__global__ __launch_bounds__(256) void shrink_mfma_kernel(
+    const typename DT::storage* __restrict__ x, const typename DT::storage* __restrict__ A_stack,
+    const int* __restrict__ seg_indptr, const int* __restrict__ adapter_ids, int S, int num_rows,
+    int num_adapters, int H1, float* __restrict__ partials, int ksplit, int h_per_split,
+    int compact) {
+    using Sh = MfmaShape<R>;
+    constexpr int T = Sh::kT;
+    constexpr int NT = Sh::kNT;
+    constexpr int NW = Sh::kNW;
+    __shared__ int s_scan[NW + 4];
+    __shared__ __align__(16) uint16_t s_a[Sh::kKcMax * R];
+    __shared__ float s_red[NW * 16 * R];
+
+    const int g = (int)(blockIdx.x / (unsigned)ksplit);
+    const int p = (int)(blockIdx.x % (unsigned)ksplit);
+    Tile tile;
+    const bool have =
+        compact ? locate_tile_compact<NT>(seg_indptr, adapter_ids, S, num_rows, num_adapters, T, g,
+                                          s_scan, tile)
+                : locate_tile<NT>(seg_indptr, adapter_ids, S, num_rows, num_adapters, T, g, s_scan,
+                                  tile);
+    if (!have) return;
+    const int h_lo = p * h_per_split;
+    const int h_hi = min(H1, h_lo + h_per_split);
+    float* out = partials + (long long)p * num_rows * R + (long long)tile.row0 * R;
+    shrink_chunk_mfma<DT, R>(A_stack + (long long)tile.adapter * H1 * R,
+                             x + (long long)tile.row0 * H1, tile.nrows, H1, h_lo, h_hi, s_a, s_red,
+                             [&](int i, int k, float v) { out[i * R + k] = v; });
+}
+
+template <typename DT, int R>
+__global__ __launch_bounds__(256) void expand_mfma_kernel(
+    typename DT::storage* __restrict__ y, const typename DT::storage* __restrict__ B_stack,
+    const int* __restrict__ seg_indptr, const int* __restrict__ adapter_ids, int S, int num_rows,
+    int num_adapters, int H2, float scale, const float* __restrict__ partials, int ksplit,
+    int csplit, int compact) {
+    using Sh = MfmaShape<R>;
+    constexpr int T = Sh::kT;
+    constexpr int NT = Sh::kNT;
+    constexpr int NW = Sh::kNW;
+    constexpr int CW = Sh::kCW;
+    __shared__ int s_scan[NW + 4];
+    __shared__ __align__(16) uint16_t s_b[Sh::kStageB];  // B chunk, then the results
+    __shared__ float s_v[T * R];
+    __shared__ __align__(16) uint16_t s_vh[T * 2 * R];
+    __shared__ float s_max[NW];
+
+    const int g = (int)(blockIdx.x / (unsigned)csplit);
+    const int c0 = (int)(blockIdx.x % (unsigned)csplit) * CW;
+    Tile tile;
+    const bool have =
+        compact ? locate_tile_compact<NT>(seg_indptr, adapter_ids, S, num_rows, num_adapters, T, g,
+                                          s_scan, tile)
+                : locate_tile<NT>(seg_indptr, adapter_ids, S, num_rows, num_adapters, T, g, s_scan,
+                                  tile);
+    if (!have) return;
+    const int nrows = tile.nrows;
+    ExpandRegs<R> er;
+    expand_prefetch<DT, R>(er, B_stack + (long long)tile.adapter * R * H2,
+                           y + (long long)tile.row0 * H2, nrows, H2, c0);
+    const long long row_stride = (long long)num_rows * R;
+    for (int t = threadIdx.x; t < T * R; t += NT) {
         const int i = t / R;
         const int k = t - i * R;
-        const float v = ldexpf(s_v[t], shift);
-        const uint32_t hi = Ops::bits(v);
-        const uint32_t lo = Ops::bits(v - Ops::value(hi));
-        s_vh[i * 2 * R + k] = (uint16_t)hi;
-        s_vh[i * 2 * R + R + k] = (uint16_t)lo;
+        s_v[t] = i < nrows
+                     ? sum_partials(partials + (long long)(tile.row0 + i) * R + k, row_stride, ksplit)
+                     : 0.f;
     }
     __syncthreads();
-
-    const float out_scale = ldexpf(scale, -shift);
-#pragma unroll
-    for (int q = 0; q < CBW; ++q) {
-        const int cb = wid * CBW + q;
-        mf32x4 acc = mf32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 2 * R / 32; ++ks) {
-            uint32_t ab[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int kr = (ks * 32 + grp * 8 + j) % R;  // hi and lo both meet B row kr
-                ab[j] = s_b[kr * CW + cb * 16 + m];
-            }
-            const uint4 bv = *reinterpret_cast<const uint4*>(s_vh + m * 2 * R + ks * 32 + grp * 8);
-            acc = Ops::mma(pack8(ab), bv, acc);
-        }
-        const int col = c0 + cb * 16 + 4 * grp;
-        if (m < nrows && col < H2) {
-            float yf[4];
-            DT::unpack2(yq[q].x, yf);
-            DT::unpack2(yq[q].y, yf + 2);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) yf[i] = fmaf(out_scale, acc[i], yf[i]);
-            store8(y + (long long)(tile.row0 + m) * H2 + col,
-                   make_uint2(DT::pack2(yf[0], yf[1]), DT::pack2(yf[2], yf[3])));
-        }
-    }
+    expand_apply<DT, R>(er, s_b, s_v, s_vh, s_max, y + (long long)tile.row0 * H2, nrows, H2, c0,
+                        scale);
 }
 
 }  // namespace sgmv

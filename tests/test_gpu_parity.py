@@ -235,15 +235,25 @@ def test_graph_replay_matches_eager():
         del junk
 
 
-@pytest.mark.parametrize("cfg", [(2, True), (4, False), (3, False)],
-                         ids=["skewed_control", "mlp_up", "prefill"])
-def test_fused_self_contained_path_is_bit_identical(cfg):
-    """With zero patience every expand workgroup of the split hand-off
-    kernel recomputes its rows' partial sums itself; the output must be
+SELF_CONTAINED_CASES = {
+    # MFMA row tiles, one long segment
+    "skewed_control": lambda: wl.config(2, control=True),
+    # vector tiles of four rows
+    "mlp_up": lambda: wl.config(4),
+    # MFMA row tiles over several segments, small enough for the single kernel
+    "prefill_small": lambda: wl.small_random(31, "f16", 2048, 2048, 16, 8, 512, 8,
+                                             allow_empty=False),
+}
+
+
+@pytest.mark.parametrize("case", list(SELF_CONTAINED_CASES))
+def test_fused_self_contained_path_is_bit_identical(case):
+    """With zero patience every expand workgroup of the single-kernel
+    hand-off recomputes its rows' partial sums itself; the output must be
     bit-identical to the normal hand-off path, and the sticky flag is set."""
     import torch
     import segmented_gather_gemv_sgmv_amd as sg
-    w = wl.config(cfg[0], control=cfg[1])
+    w = SELF_CONTAINED_CASES[case]()
     d = to_device(w)
     ws = torch.zeros(sg.lora_apply_workspace_bytes(w.num_rows, w.num_segments, w.H1, w.H2, w.r,
                                                    torch_dtype(w.dtype)),
@@ -287,6 +297,22 @@ def test_workspace_reused_across_shapes():
         y_ref, _ = oracle.lora_apply(w.y0, w.x, w.A, w.B, w.seg_indptr, w.adapter_ids, w.scale)
         assert_close(y.double().cpu().numpy(), y_ref, w.dtype, w.name)
         assert int(ws[:262144].view(torch.int32).abs().sum()) == 0
+
+
+@pytest.mark.parametrize("seed,dtype,H1,H2,r,N,R,S,tail", [
+    (41, "bf16", 1024, 3072, 64, 7, 3000, 5, 0),
+    (42, "f16", 512, 1024, 128, 4, 2000, 3, 37),
+])
+def test_two_launch_mfma_path(seed, dtype, H1, H2, r, N, R, S, tail):
+    """Row-heavy calls too large for one resident round of single-kernel
+    items run as a shrink launch and an expand launch; ragged segments
+    (some empty) and rows outside every segment included."""
+    w = wl.small_random(seed, dtype, H1, H2, r, N, R, S, uncovered_tail=tail)
+    y_ref, _ = oracle.lora_apply(w.y0, w.x, w.A, w.B, w.seg_indptr, w.adapter_ids, w.scale)
+    y = gpu_lora_apply(w)
+    assert_close(y, y_ref, dtype, w.name)
+    if tail:
+        assert np.array_equal(y[R - tail:], w.y0[R - tail:].astype(y.dtype))
 
 
 @pytest.mark.parametrize("S,R,lengths_kind", [(1500, 1500, "ones"), (1300, 700, "sparse"),
