@@ -188,6 +188,26 @@ def cpu_baseline(w, budget_s: float = 10.0):
                        f"({el:.1f} s, one thread)")
 
 
+# Timed workloads by name: the decode projection the metric is quoted on, and
+# the other seeded configurations (each a lora_apply call of its own shape).
+WORKLOADS = {
+    "llama7b_decode": lambda wl: wl.llama7b_decode(seed=0),
+    "skewed_decode": lambda wl: wl.skewed_decode(seed=0),
+    "skewed_decode_control": lambda wl: wl.skewed_decode(seed=0, control=True),
+    "prefill": lambda wl: wl.prefill(seed=0),
+    "mlp_up_decode": lambda wl: wl.mlp_up_decode(seed=0),
+    "tiny": lambda wl: wl.tiny(seed=0),
+}
+WORKLOAD_SHAPES = {
+    "llama7b_decode": "Llama-2-7B decode shapes",
+    "skewed_decode": "Llama-2-7B shapes, Zipf segment lengths",
+    "skewed_decode_control": "Llama-2-7B shapes, one segment",
+    "prefill": "Llama-2-7B prefill shapes",
+    "mlp_up_decode": "Llama-13B up-projection decode shapes",
+    "tiny": "tiny shapes",
+}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -197,6 +217,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain BYTES-sized device copy (counter calibration)")
+    ap.add_argument("--workload", default="llama7b_decode", choices=sorted(WORKLOADS),
+                    help="workload to time (default: the Llama-2-7B decode projection); the "
+                         "others are the remaining seeded configurations")
     args = ap.parse_args(argv)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
@@ -214,7 +237,7 @@ def main(argv=None):
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
 
-    w = wl.llama7b_decode(seed=0)
+    w = WORKLOADS[args.workload](wl)
     res = run_gpu(w, args.steps, args.warmup)
     step_s = res["gpu_ms"] / 1e3 / args.steps
     rows = int(w.seg_lengths.sum())
@@ -232,8 +255,8 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
-        "data": "synthetic (seeded; Llama-2-7B decode shapes, no weights)",
+        "dtype": w.dtype,
+        "data": "synthetic (seeded; " + WORKLOAD_SHAPES[args.workload] + ", no weights)",
         "config": {
             "workload": w.name, "H1": w.H1, "H2": w.H2, "r": w.r, "rows": rows,
             "segments": w.num_segments, "adapters_in_stack": w.num_adapters, "scale": w.scale,
@@ -244,7 +267,8 @@ def main(argv=None):
         "hbm_peak_frac": achieved / HBM_PEAK_GBPS,
         "roofline": {
             "bound": "hbm",
-            "kernel": "lora_fused_kernel (one launch per step)",
+            "kernel": ("lora_fused_kernel (one launch per step)" if args.workload == "llama7b_decode"
+                       else "every launch of one lora_apply call"),
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
