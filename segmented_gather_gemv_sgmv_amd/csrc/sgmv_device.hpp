@@ -186,7 +186,13 @@ __device__ __forceinline__ SegBounds seg_bounds(const int* __restrict__ seg_indp
     return b;
 }
 
-// `lds` must hold at least NT/64 + 4 ints.  Every thread of the block must
+// LDS a tile lookup needs: the scan's per-wave totals and what the owning
+// thread found (segment, tile index, bounds, adapter), so that nobody has
+// to read the table again after the scan.
+template <int NT>
+constexpr int tile_scan_ints() { return NT / kWave + 8; }
+
+// `lds` must hold tile_scan_ints<NT>() ints.  Every thread of the block must
 // call this (it synchronises the block when g >= S).
 template <int NT>
 __device__ __forceinline__ bool locate_tile(const int* __restrict__ seg_indptr,
@@ -203,7 +209,7 @@ __device__ __forceinline__ bool locate_tile(const int* __restrict__ seg_indptr,
         return true;
     }
     const int q = g - S;  // index among the non-first tiles
-    int* found = lds + NT / kWave;  // [0] = segment, [1] = tile index in segment
+    int* found = lds + NT / kWave;  // segment, tile index in segment, lo, hi, adapter
     if (threadIdx.x == 0) found[0] = -1;
     __syncthreads();
     int running = 0;  // non-first tiles in the segments already scanned
@@ -218,8 +224,12 @@ __device__ __forceinline__ bool locate_tile(const int* __restrict__ seg_indptr,
         const int incl = block_inclusive_scan<NT>(extra, lds, total);
         const int excl = running + incl - extra;
         if (extra > 0 && q >= excl && q < excl + extra) {
+            const SegBounds b = seg_bounds(seg_indptr, adapter_ids, s, num_rows, num_adapters);
             found[0] = s;
             found[1] = q - excl + 1;
+            found[2] = b.lo;
+            found[3] = b.hi;
+            found[4] = adapter_ids[s];
         }
         running += total;
         if (q < running) break;  // uniform: running and q are block-uniform
@@ -227,11 +237,10 @@ __device__ __forceinline__ bool locate_tile(const int* __restrict__ seg_indptr,
     __syncthreads();
     const int s = found[0];
     if (s < 0) return false;
-    const SegBounds b = seg_bounds(seg_indptr, adapter_ids, s, num_rows, num_adapters);
     out.seg = s;
-    out.row0 = b.lo + found[1] * T;
-    out.nrows = min(T, b.hi - out.row0);
-    out.adapter = adapter_ids[s];
+    out.row0 = found[2] + found[1] * T;
+    out.nrows = min(T, found[3] - out.row0);
+    out.adapter = found[4];
     return true;
 }
 
@@ -240,7 +249,8 @@ __device__ __forceinline__ bool locate_tile(const int* __restrict__ seg_indptr,
 // per-segment tile counts.  A segment table with S segments over R rows has
 // at most m + floor((R - m) / T) tiles, m = min(S, R) (each non-empty
 // segment of n rows has 1 + floor((n - 1) / T) tiles), so a launch needs no
-// slot that finds nothing.  Every thread of the block must call this.
+// slot that finds nothing.  `lds` must hold tile_scan_ints<NT>() ints.
+// Every thread of the block must call this.
 template <int NT>
 __device__ __forceinline__ bool locate_tile_compact(const int* __restrict__ seg_indptr,
                                                     const int* __restrict__ adapter_ids, int S,
@@ -250,13 +260,14 @@ __device__ __forceinline__ bool locate_tile_compact(const int* __restrict__ seg_
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = threadIdx.x / kWave;
     int* wave_tot = lds;            // [NW]
-    int* found = lds + NW;          // [0] = segment, [1] = tile index in segment
+    int* found = lds + NW;          // segment, tile index in segment, lo, hi, adapter
     int running = 0;                // tiles in the segments already scanned
     for (int base = 0; base < S; base += NT) {
         const int s = base + (int)threadIdx.x;
         int cnt = 0;
+        SegBounds b{0, 0, false};
         if (s < S) {
-            const SegBounds b = seg_bounds(seg_indptr, adapter_ids, s, num_rows, num_adapters);
+            b = seg_bounds(seg_indptr, adapter_ids, s, num_rows, num_adapters);
             if (b.ok) cnt = (b.hi - b.lo + T - 1) / T;
         }
         const int incl_w = wave_inclusive_scan(cnt, lane);
@@ -274,18 +285,19 @@ __device__ __forceinline__ bool locate_tile_compact(const int* __restrict__ seg_
         if (cnt > 0 && g >= excl && g < excl + cnt) {
             found[0] = s;
             found[1] = g - excl;
+            found[2] = b.lo;
+            found[3] = b.hi;
+            found[4] = adapter_ids[s];
         }
         running += total;
         __syncthreads();  // found[] visible; wave_tot[] free for the next pass
         if (g < running) break;  // block-uniform
     }
     if (g >= running) return false;  // fewer tiles than g + 1
-    const int s = found[0];
-    const SegBounds b = seg_bounds(seg_indptr, adapter_ids, s, num_rows, num_adapters);
-    out.seg = s;
-    out.row0 = b.lo + found[1] * T;
-    out.nrows = min(T, b.hi - out.row0);
-    out.adapter = adapter_ids[s];
+    out.seg = found[0];
+    out.row0 = found[2] + found[1] * T;
+    out.nrows = min(T, found[3] - out.row0);
+    out.adapter = found[4];
     return true;
 }
 

@@ -243,7 +243,7 @@ __global__ __launch_bounds__(NT) void lora_fused_kernel(
     constexpr int N = RB * VEC;
     static_assert(R % KB == 0, "KB must divide R");
 
-    __shared__ int s_scan[NT / kWave + 4];
+    __shared__ int s_scan[tile_scan_ints<NT>()];
     __shared__ float s_red[NW * LPR * N];
     __shared__ float s_v[RB * R];
     __shared__ int s_flag;

@@ -113,7 +113,7 @@ __global__ __launch_bounds__(NT) void shrink_vec_kernel(
     constexpr int N = RB * VEC;         // accumulators per lane
     using RS = ReduceScatter<N, LPR>;
 
-    __shared__ int s_scan[NT / kWave + 4];
+    __shared__ int s_scan[tile_scan_ints<NT>()];
     __shared__ float s_red[NW][LPR * N];
 
     const int g = blockIdx.x / ksplit;
@@ -202,7 +202,7 @@ __global__ __launch_bounds__(kWave) void expand_vec_kernel(
     constexpr int CW = kWave * VEC;
     static_assert(R % KB == 0, "KB must divide the rank");
 
-    __shared__ int s_scan[1 + 4];
+    __shared__ int s_scan[tile_scan_ints<kWave>()];
     __shared__ float s_v[RB][R];
 
     const int g = blockIdx.x / csplit;
@@ -288,7 +288,7 @@ __global__ __launch_bounds__(NT) void shrink_generic_kernel(
     const int* __restrict__ adapter_ids, int S, int num_rows, int num_adapters, int H1, int r,
     int ksplit, int h_per_split) {
     using st = typename DT::storage;
-    __shared__ int s_scan[NT / kWave + 4];
+    __shared__ int s_scan[tile_scan_ints<NT>()];
     __shared__ float s_red[NT * RB];
 
     const int g = blockIdx.x / ksplit;
@@ -337,7 +337,7 @@ __global__ __launch_bounds__(NT) void expand_generic_kernel(
     const int* __restrict__ adapter_ids, int S, int num_rows, int num_adapters, int r, int H2,
     float scale, int csplit) {
     using st = typename DT::storage;
-    __shared__ int s_scan[NT / kWave + 4];
+    __shared__ int s_scan[tile_scan_ints<NT>()];
     __shared__ float s_v[RB * 128];
 
     const int g = blockIdx.x / csplit;

@@ -85,15 +85,16 @@ struct MfmaShape {
     static constexpr int kCW = (8192 / R) < 512 ? (8192 / R) : 512;  // expand columns per item
     static constexpr int kCBW = kCW / (16 * kNW);        // 16-column blocks per wave
     static constexpr int kBV = R * kCW / 8 / kNT;        // 16-byte B vectors per thread
-    // Epilogue: the tile's results (16 x kCW floats) go through LDS so that y
-    // is read and written in row-contiguous 16-byte pieces: kYU pieces of 8
-    // columns per thread (a wave covers 512 columns).  In LDS, float4 f of
-    // row i sits at position f ^ (i & 15), so that neither the MFMA-layout
-    // writes nor the row reads meet bank conflicts.
+    // Epilogue: y is read and written in row-contiguous 16-byte pieces (kYU
+    // pieces of 8 columns per thread; a wave covers 512 columns of a row),
+    // and the 16 x kCW tile of y passes through LDS (over the B chunk, which
+    // is at least as large) to meet the MFMA result layout.  In LDS, the
+    // 8-byte group g of row i sits at position g ^ (i & 15), so that neither
+    // the row-piece accesses nor the MFMA-layout ones meet bank conflicts.
     static constexpr int kYU = (2 * kCW + kNT - 1) / kNT;
-    // LDS (in 16-bit units) of the B chunk, reused for the results
-    static constexpr int kStageB = R * kCW > 2 * kT * kCW ? R * kCW : 2 * kT * kCW;
-    static_assert(kCW % 64 == 0, "the swizzle needs at least 16 float4 per row");
+    static constexpr int kStageB = R * kCW;  // LDS of the B chunk, in 16-bit units
+    static_assert(kStageB >= kT * kCW, "the y tile must fit over the B chunk");
+    static_assert(kCW % 64 == 0, "the swizzle needs at least 16 groups per row");
     static_assert(kBV * kNT * 8 == R * kCW, "B chunk must split evenly over the threads");
     static_assert(R % 16 == 0 && R <= 128, "MFMA path needs r in {16, 32, 64, 128}");
 };
@@ -287,34 +288,46 @@ __device__ __forceinline__ void expand_apply(const ExpandRegs<R>& e, uint16_t* s
             acc[q] = Ops::mma(pack8(ab), bv, acc[q]);
         }
     }
-    // Results to LDS over the B chunk (every wave is done with it), lane
-    // (m, grp) holding columns cb * 16 + 4 grp + [0, 4) of row m.
+    // The y tile, as loaded (row pieces), into LDS over the B chunk: every
+    // wave is done with B once the barrier is passed.
     __syncthreads();
-    float* s_y = reinterpret_cast<float*>(s_b);
-#pragma unroll
-    for (int q = 0; q < CBW; ++q) {
-        const int f = (wid * CBW + q) * 4 + grp;  // float4 index of columns cb * 16 + 4 grp
-        *reinterpret_cast<float4*>(s_y + m * CW + ((f ^ m) << 2)) =
-            make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
-    }
-    __syncthreads();
-    // y += scale * result, 8 columns of one row per piece.
+    uint2* s_y = reinterpret_cast<uint2*>(s_b);  // [16][kCW / 4] groups of 4 columns
+    constexpr int G = CW / 4;                    // 8-byte groups per row
 #pragma unroll
     for (int j = 0; j < Sh::kYU; ++j) {
         const int u = tid + j * NT;
         const int row = u / (CW / 8);
-        const int cl = (u % (CW / 8)) * 8;
-        if (u < 2 * CW && row < nrows && c0 + cl < H2) {
-            const int f = cl >> 2;
-            const float4 r0 = *reinterpret_cast<const float4*>(s_y + row * CW + ((f ^ row) << 2));
-            const float4 r1 =
-                *reinterpret_cast<const float4*>(s_y + row * CW + (((f + 1) ^ row) << 2));
-            const float rv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-            float yf[8];
-            DT::unpack(e.yv[j], yf);
+        const int g = (u % (CW / 8)) * 2;
+        if (u < 2 * CW) {
+            s_y[row * G + (g ^ row)] = make_uint2(e.yv[j].x, e.yv[j].y);
+            s_y[row * G + ((g + 1) ^ row)] = make_uint2(e.yv[j].z, e.yv[j].w);
+        }
+    }
+    __syncthreads();
+    // Lane (m, grp) owns columns cb * 16 + 4 grp + [0, 4) of row m: one group.
 #pragma unroll
-            for (int i = 0; i < 8; ++i) yf[i] = fmaf(out_scale, rv[i], yf[i]);
-            store16(yr + (long long)row * H2 + c0 + cl, DT::pack(yf));
+    for (int q = 0; q < CBW; ++q) {
+        const int g = (wid * CBW + q) * 4 + grp;
+        uint2* slot = &s_y[m * G + (g ^ m)];
+        const uint2 old = *slot;
+        float yf[4];
+        DT::unpack2(old.x, yf);
+        DT::unpack2(old.y, yf + 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) yf[i] = fmaf(out_scale, acc[q][i], yf[i]);
+        *slot = make_uint2(DT::pack2(yf[0], yf[1]), DT::pack2(yf[2], yf[3]));
+    }
+    __syncthreads();
+    // The updated tile back to y, row pieces of 8 columns.
+#pragma unroll
+    for (int j = 0; j < Sh::kYU; ++j) {
+        const int u = tid + j * NT;
+        const int row = u / (CW / 8);
+        const int g = (u % (CW / 8)) * 2;
+        if (u < 2 * CW && row < nrows && c0 + g * 4 < H2) {
+            const uint2 a0 = s_y[row * G + (g ^ row)];
+            const uint2 a1 = s_y[row * G + ((g + 1) ^ row)];
+            store16(yr + (long long)row * H2 + c0 + g * 4, make_uint4(a0.x, a0.y, a1.x, a1.y));
         }
     }
 }
@@ -335,7 +348,7 @@ __global__ __launch_bounds__(256) void lora_mfma_kernel(
     constexpr int NW = Sh::kNW;
     constexpr int CW = Sh::kCW;
 
-    __shared__ int s_scan[NW + 4];
+    __shared__ int s_scan[tile_scan_ints<NT>()];
     // A chunk; later the B chunk [R][CW] and then the expand results
     __shared__ __align__(16) uint16_t s_a[Sh::kKcMax * R > Sh::kStageB ? Sh::kKcMax * R
                                                                        : Sh::kStageB];
@@ -437,7 +450,7 @@ __global__ __launch_bounds__(256) void shrink_mfma_kernel(
     constexpr int T = Sh::kT;
     constexpr int NT = Sh::kNT;
     constexpr int NW = Sh::kNW;
-    __shared__ int s_scan[NW + 4];
+    __shared__ int s_scan[tile_scan_ints<NT>()];
     __shared__ __align__(16) uint16_t s_a[Sh::kKcMax * R];
     __shared__ float s_red[NW * 16 * R];
 
@@ -469,7 +482,7 @@ __global__ __launch_bounds__(256) void expand_mfma_kernel(
     constexpr int NT = Sh::kNT;
     constexpr int NW = Sh::kNW;
     constexpr int CW = Sh::kCW;
-    __shared__ int s_scan[NW + 4];
+    __shared__ int s_scan[tile_scan_ints<NT>()];
     __shared__ __align__(16) uint16_t s_b[Sh::kStageB];  // B chunk, then the results
     __shared__ float s_v[T * R];
     __shared__ __align__(16) uint16_t s_vh[T * 2 * R];
