@@ -179,6 +179,47 @@ int sgmv_set_fused_wait(double seconds);
 int sgmv_validate_segments(const int32_t* h_seg_indptr, const int32_t* h_adapter_ids,
                            int32_t num_segments, int32_t num_rows, int32_t num_adapters);
 
+/*
+ * Segment tables built on the device from per-row adapter ids (the
+ * per-sample LoRA indices of Punica walkthrough, omica.com.cn/news/959180,
+ * section 3.2; SGMV itself wants the batch "segmented" by adapter, Punica
+ * review, nubint.ai, "Proposed method").
+ *
+ * row_ids [num_rows] int32: the adapter of each row; an id outside
+ * [0, num_adapters) means "no adapter" (the row is left untouched by a
+ * lora_apply over the resulting table).
+ *
+ * Outputs, all DEVICE arrays owned by the caller:
+ *   seg_indptr [num_rows + 1], adapter_ids [num_rows]: a segment table of
+ *     num_rows segments whose first *num_segments are the real ones; the
+ *     rest are empty (seg_indptr = the end of the last real segment,
+ *     adapter id -1).  So the table can be handed to lora_apply with
+ *     num_segments = num_rows and no device-to-host read.
+ *   num_segments [1]: the real segment count.
+ *
+ * sgmv_build_segments: one segment per maximal run of equal (normalised)
+ * ids, in row order; no reordering of rows is needed.  Rows without an
+ * adapter form segments with adapter id -1.
+ *
+ * sgmv_group_rows: also writes perm [num_rows], a stable grouping of the
+ * rows: the rows of adapter 0 in increasing row order, then those of
+ * adapter 1, ..., then the rows without an adapter.  Row j of the grouped
+ * batch is row perm[j] of the original one.  The segment table describes
+ * the grouped batch, with one segment per adapter present, in increasing
+ * id order; the rows without an adapter come after the last segment.
+ * num_adapters must be at most 4096 (SGMV_ERR_UNSUPPORTED beyond).
+ *
+ * Both run as one workgroup on `stream` and return SGMV_OK after
+ * enqueueing, SGMV_ERR_NULL_PTR / SGMV_ERR_BAD_SHAPE for bad arguments, or
+ * SGMV_ERR_HIP.  num_rows == 0 writes seg_indptr[0] = 0 and a zero count.
+ */
+int sgmv_build_segments(const int32_t* row_ids, int32_t num_rows, int32_t num_adapters,
+                        int32_t* seg_indptr, int32_t* adapter_ids, int32_t* num_segments,
+                        void* stream);
+int sgmv_group_rows(const int32_t* row_ids, int32_t num_rows, int32_t num_adapters,
+                    int32_t* perm, int32_t* seg_indptr, int32_t* adapter_ids,
+                    int32_t* num_segments, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

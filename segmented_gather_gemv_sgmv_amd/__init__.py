@@ -50,6 +50,8 @@ ABI = [
                                   _i32, _f32, _i32, _vp, _sz, _vp]),
     ("sgmv_set_fused_wait", ctypes.c_int, [ctypes.c_double]),
     ("sgmv_validate_segments", ctypes.c_int, [_vp, _vp, _i32, _i32, _i32]),
+    ("sgmv_build_segments", ctypes.c_int, [_vp, _i32, _i32, _vp, _vp, _vp, _vp]),
+    ("sgmv_group_rows", ctypes.c_int, [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
 ]
 
 
@@ -260,7 +262,49 @@ def validate_segments(seg_indptr, adapter_ids, num_rows, num_adapters) -> int:
                                             ids.shape[0], num_rows, num_adapters))
 
 
+def build_segments(row_ids, num_adapters: int):
+    """Segment table from per-row adapter ids (int32 device tensor), one
+    segment per maximal run of equal ids.  Returns ``(seg_indptr,
+    adapter_ids, num_segments)``: tables of ``num_rows + 1`` / ``num_rows``
+    entries whose tail describes empty segments (so they can go straight to
+    ``lora_apply``) and a one-element device tensor with the real count."""
+    torch = _torch()
+    dev = row_ids.device
+    _need(row_ids, "row_ids", dev, torch.int32, 1)
+    R = row_ids.numel()
+    seg = torch.empty(R + 1, dtype=torch.int32, device=dev)
+    ids = torch.empty(R, dtype=torch.int32, device=dev)
+    count = torch.empty(1, dtype=torch.int32, device=dev)
+    _check(lib().sgmv_build_segments(row_ids.data_ptr() if R else None, R, int(num_adapters),
+                                     seg.data_ptr(), ids.data_ptr() if R else None,
+                                     count.data_ptr(), _stream_ptr(dev)),
+           "sgmv_build_segments")
+    return seg, ids, count
+
+
+def group_rows(row_ids, num_adapters: int):
+    """Stable grouping of rows by adapter (int32 device tensor of per-row
+    ids).  Returns ``(perm, seg_indptr, adapter_ids, num_segments)``: row j
+    of the grouped batch is row ``perm[j]``; the table describes the grouped
+    batch with one segment per adapter present (tail entries empty)."""
+    torch = _torch()
+    dev = row_ids.device
+    _need(row_ids, "row_ids", dev, torch.int32, 1)
+    R = row_ids.numel()
+    perm = torch.empty(R, dtype=torch.int32, device=dev)
+    seg = torch.empty(R + 1, dtype=torch.int32, device=dev)
+    ids = torch.empty(R, dtype=torch.int32, device=dev)
+    count = torch.empty(1, dtype=torch.int32, device=dev)
+    _check(lib().sgmv_group_rows(row_ids.data_ptr() if R else None, R, int(num_adapters),
+                                 perm.data_ptr() if R else None, seg.data_ptr(),
+                                 ids.data_ptr() if R else None, count.data_ptr(),
+                                 _stream_ptr(dev)),
+           "sgmv_group_rows")
+    return perm, seg, ids, count
+
+
 __all__ = [
+    "build_segments", "group_rows",
     "lora_apply", "sgmv_shrink", "sgmv_expand", "lora_apply_workspace_bytes",
     "shrink_workspace_bytes", "validate_segments", "set_fused_wait", "lib", "SGMVError", "ABI", "LIBRARY",
 ]

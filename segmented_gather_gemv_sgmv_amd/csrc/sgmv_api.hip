@@ -20,6 +20,7 @@
 #include "sgmv_gemv.hpp"
 #include "sgmv_fused.hpp"
 #include "sgmv_mfma.hpp"
+#include "sgmv_segments.hpp"
 
 namespace {
 
@@ -652,6 +653,30 @@ int sgmv_set_fused_wait(double seconds) {
     }
     g_wait_bits.store(b, std::memory_order_relaxed);
     return SGMV_OK;
+}
+
+int sgmv_build_segments(const int32_t* row_ids, int32_t num_rows, int32_t num_adapters,
+                        int32_t* seg_indptr, int32_t* adapter_ids, int32_t* num_segments,
+                        void* stream) {
+    if (num_rows < 0 || num_adapters < 0) return SGMV_ERR_BAD_SHAPE;
+    if (!seg_indptr || !num_segments || (num_rows > 0 && (!row_ids || !adapter_ids)))
+        return SGMV_ERR_NULL_PTR;
+    launch(&build_segments_kernel, dim3(1), dim3(kSegThreads), (hipStream_t)stream, row_ids,
+           num_rows, num_adapters, seg_indptr, adapter_ids, num_segments);
+    return launch_status();
+}
+
+int sgmv_group_rows(const int32_t* row_ids, int32_t num_rows, int32_t num_adapters,
+                    int32_t* perm, int32_t* seg_indptr, int32_t* adapter_ids,
+                    int32_t* num_segments, void* stream) {
+    if (num_rows < 0 || num_adapters < 0) return SGMV_ERR_BAD_SHAPE;
+    if (num_adapters > kGroupMaxAdapters) return SGMV_ERR_UNSUPPORTED;
+    if (!seg_indptr || !num_segments ||
+        (num_rows > 0 && (!row_ids || !adapter_ids || !perm)))
+        return SGMV_ERR_NULL_PTR;
+    launch(&group_rows_kernel, dim3(1), dim3(kSegThreads), (hipStream_t)stream, row_ids, num_rows,
+           num_adapters, perm, seg_indptr, adapter_ids, num_segments);
+    return launch_status();
 }
 
 int sgmv_validate_segments(const int32_t* h_seg_indptr, const int32_t* h_adapter_ids,
