@@ -118,3 +118,27 @@ def test_lora_apply_from_per_row_ids(dtype, H1, H2, r, N, R):
     assert_close(y.double().cpu().numpy(), y_ref, dtype, "grouped table")
     invalid = (row_ids < 0) | (row_ids >= N)
     assert np.array_equal(y.double().cpu().numpy()[invalid], w.y0[invalid].astype(np.float64))
+
+
+@pytest.mark.parametrize("group", [False, True], ids=["runs", "grouped"])
+def test_lora_linear_module(group):
+    """LoRALinear = torch's dense linear for the base product plus the SGMV
+    add-on for per-row adapters: its output equals the oracle's add-on
+    applied to that same base output."""
+    import torch
+    from segmented_gather_gemv_sgmv_amd.lora_linear import LoRALinear
+    R, H1, H2, r, N = 96, 512, 384, 16, 5
+    w = wl.small_random(77, "f16", H1, H2, r, N, R, 1)
+    rng = np.random.default_rng(5)
+    weight = torch.tensor(rng.normal(0, 0.05, size=(H2, H1)), dtype=torch.float16, device="cuda")
+    bias = torch.tensor(rng.normal(0, 1, size=H2), dtype=torch.float16, device="cuda")
+    row_ids = rng.integers(-1, N, size=R)
+    d = to_device(w)
+    layer = LoRALinear(weight, d["A"], d["B"], scale=w.scale, bias=bias, group=group)
+    y = layer(d["x"], _dev(row_ids))
+    base = torch.nn.functional.linear(d["x"], weight, bias)
+    torch.cuda.synchronize()
+    wb = wl.Workload(w.name, w.dtype, H1, H2, r, N, w.seg_indptr, w.adapter_ids, w.scale, w.x,
+                     w.A, w.B, base.float().cpu().numpy())
+    y_ref = _reference(wb, row_ids.tolist())
+    assert_close(y.double().cpu().numpy(), y_ref, "f16", "LoRALinear")
