@@ -206,8 +206,11 @@ int sgmv_validate_segments(const int32_t* h_seg_indptr, const int32_t* h_adapter
  * adapter 1, ..., then the rows without an adapter.  Row j of the grouped
  * batch is row perm[j] of the original one.  The segment table describes
  * the grouped batch, with one segment per adapter present, in increasing
- * id order; the rows without an adapter come after the last segment.
- * num_adapters must be at most 4096 (SGMV_ERR_UNSUPPORTED beyond).
+ * id order; the rows without an adapter come after the last segment.  Its
+ * size is M = min(num_rows, num_adapters) segments instead of num_rows
+ * (seg_indptr [M + 1], adapter_ids [M] are written), since there is at most
+ * one segment per adapter; pass M to lora_apply.  num_adapters must be at
+ * most 4096 (SGMV_ERR_UNSUPPORTED beyond).
  *
  * Both run as one workgroup on `stream` and return SGMV_OK after
  * enqueueing, SGMV_ERR_NULL_PTR / SGMV_ERR_BAD_SHAPE for bad arguments, or

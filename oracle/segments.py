@@ -15,8 +15,9 @@ definitions, written as loops over the rows:
 
 Reading taken (the pages do not say): an id outside [0, num_adapters) means
 "no adapter"; such a row belongs to no segment of the grouped table and to
-segments with adapter id -1 in the run table.  Both return tables padded to
-``num_rows`` segments with empty ones, the form the device builders write.
+segments with adapter id -1 in the run table.  The tables are padded with
+empty segments to ``num_rows`` (runs) or ``min(num_rows, num_adapters)``
+(grouping) entries, the form the device builders write.
 """
 from __future__ import annotations
 
@@ -42,8 +43,8 @@ def build_segments(row_ids, num_adapters: int):
 
 
 def group_rows(row_ids, num_adapters: int):
-    """Stable grouping.  Returns (perm [R], seg_indptr [R+1],
-    adapter_ids [R], count)."""
+    """Stable grouping.  Returns (perm [R], seg_indptr [M+1],
+    adapter_ids [M], count) with M = min(R, num_adapters)."""
     ids = [_norm(int(a), num_adapters) for a in row_ids]
     R = len(ids)
     rows_of = {}
@@ -57,6 +58,7 @@ def group_rows(row_ids, num_adapters: int):
     grouped = len(perm)
     perm.extend(rows_of.get(-1, []))
     count = len(aid)
-    seg += [grouped] * (R + 1 - count)
-    aid += [-1] * (R - count)
+    M = min(R, num_adapters)  # at most one segment per adapter
+    seg += [grouped] * (M + 1 - count)
+    aid += [-1] * (M - count)
     return perm, seg, aid, count

@@ -286,18 +286,20 @@ def group_rows(row_ids, num_adapters: int):
     """Stable grouping of rows by adapter (int32 device tensor of per-row
     ids).  Returns ``(perm, seg_indptr, adapter_ids, num_segments)``: row j
     of the grouped batch is row ``perm[j]``; the table describes the grouped
-    batch with one segment per adapter present (tail entries empty)."""
+    batch with one segment per adapter present, padded with empty segments
+    to min(num_rows, num_adapters) entries."""
     torch = _torch()
     dev = row_ids.device
     _need(row_ids, "row_ids", dev, torch.int32, 1)
     R = row_ids.numel()
+    M = min(R, max(int(num_adapters), 0))
     perm = torch.empty(R, dtype=torch.int32, device=dev)
-    seg = torch.empty(R + 1, dtype=torch.int32, device=dev)
-    ids = torch.empty(R, dtype=torch.int32, device=dev)
+    seg = torch.empty(M + 1, dtype=torch.int32, device=dev)
+    ids = torch.empty(M, dtype=torch.int32, device=dev)
     count = torch.empty(1, dtype=torch.int32, device=dev)
     _check(lib().sgmv_group_rows(row_ids.data_ptr() if R else None, R, int(num_adapters),
                                  perm.data_ptr() if R else None, seg.data_ptr(),
-                                 ids.data_ptr() if R else None, count.data_ptr(),
+                                 ids.data_ptr() if M else None, count.data_ptr(),
                                  _stream_ptr(dev)),
            "sgmv_group_rows")
     return perm, seg, ids, count

@@ -671,8 +671,8 @@ int sgmv_group_rows(const int32_t* row_ids, int32_t num_rows, int32_t num_adapte
                     int32_t* num_segments, void* stream) {
     if (num_rows < 0 || num_adapters < 0) return SGMV_ERR_BAD_SHAPE;
     if (num_adapters > kGroupMaxAdapters) return SGMV_ERR_UNSUPPORTED;
-    if (!seg_indptr || !num_segments ||
-        (num_rows > 0 && (!row_ids || !adapter_ids || !perm)))
+    if (!seg_indptr || !num_segments || (num_rows > 0 && (!row_ids || !perm)) ||
+        (num_rows > 0 && num_adapters > 0 && !adapter_ids))
         return SGMV_ERR_NULL_PTR;
     launch(&group_rows_kernel, dim3(1), dim3(kSegThreads), (hipStream_t)stream, row_ids, num_rows,
            num_adapters, perm, seg_indptr, adapter_ids, num_segments);

@@ -18,7 +18,9 @@
 // are in no segment of the grouped table, and form segments with adapter id
 // -1 (which lora_apply skips) in the run table.  Entries of the output
 // arrays past the real segment count describe empty segments, so a caller
-// may pass num_rows as the segment count without reading the count back.
+// may pass the table's size -- num_rows for runs, min(num_rows,
+// num_adapters) for the grouping -- as the segment count without reading
+// the count back.
 #pragma once
 
 #include "sgmv_device.hpp"
@@ -109,9 +111,10 @@ __global__ __launch_bounds__(kSegThreads) void group_rows_kernel(
     }
     __syncthreads();
     const int grouped = s_off[num_adapters];  // rows with a valid adapter
-    for (int k = segs + tid; k <= num_rows; k += kSegThreads) {
+    const int smax = min(num_rows, num_adapters);  // table size: at most one segment per adapter
+    for (int k = segs + tid; k <= smax; k += kSegThreads) {
         seg_indptr[k] = grouped;
-        if (k < num_rows) adapter_ids[k] = -1;
+        if (k < smax) adapter_ids[k] = -1;
     }
     if (tid == 0) *num_segments = segs;
 

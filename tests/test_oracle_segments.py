@@ -47,9 +47,10 @@ def check_grouped(row_ids, N, perm, seg, aid, count):
     norm = [a if 0 <= a < N else -1 for a in row_ids]
     assert sorted(perm) == list(range(R)), "perm is a permutation"
     grouped = sum(1 for a in norm if a >= 0)
-    assert len(seg) == R + 1 and len(aid) == R
-    assert all(seg[k] == grouped for k in range(count, R + 1))
-    assert all(aid[k] == -1 for k in range(count, R))
+    M = min(R, N)
+    assert len(seg) == M + 1 and len(aid) == M
+    assert all(seg[k] == grouped for k in range(count, M + 1))
+    assert all(aid[k] == -1 for k in range(count, M))
     assert [aid[k] for k in range(count)] == sorted(set(a for a in norm if a >= 0))
     assert seg[0] == 0
     for k in range(count):
