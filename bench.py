@@ -28,6 +28,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -57,7 +59,7 @@ def algorithmic_flops(w) -> int:
 class BenchState:
     """Device copies of a workload, rotated over `nsets` buffer sets."""
 
-    def __init__(self, w, nsets: int, device="cuda:0"):
+    def __init__(self, w, nsets: int, device="cuda:0", row_ids=None):
         import torch
         import segmented_gather_gemv_sgmv_amd as sg
         self.w = w
@@ -76,12 +78,30 @@ class BenchState:
             self.sets.append(s)
         self.y0 = base["y0"]
         nbytes = sg.lora_apply_workspace_bytes(w.num_rows, w.num_segments, w.H1, w.H2, w.r, dt)
-        self.workspace = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
         self.device = dev
+        self.row_ids_mode = row_ids
+        if row_ids:
+            # Per-row adapter ids (the rows of the workload are already grouped,
+            # so both builders return the workload's own segments).
+            R, N = w.num_rows, w.num_adapters
+            per_row = np.full(R, -1, dtype=np.int32)
+            for k in range(w.num_segments):
+                per_row[w.seg_indptr[k]:w.seg_indptr[k + 1]] = w.adapter_ids[k]
+            self.row_ids = torch.from_numpy(per_row).to(dev)
+            M = R if row_ids == "runs" else min(R, N)
+            self.built = [torch.empty(n, dtype=torch.int32, device=dev)
+                          for n in ((R + 1, R, 1) if row_ids == "runs" else (R, M + 1, M, 1))]
+            nbytes = max(nbytes, sg.lora_apply_workspace_bytes(R, M, w.H1, w.H2, w.r, dt))
+        self.workspace = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
 
     def step(self, i: int):
         s = self.sets[i % len(self.sets)]
-        self.sg.lora_apply(s["y"], s["x"], s["A"], s["B"], self.seg, self.ids, self.w.scale,
+        seg, ids = self.seg, self.ids
+        if self.row_ids_mode == "runs":
+            seg, ids, _ = self.sg.build_segments(self.row_ids, self.w.num_adapters, out=self.built)
+        elif self.row_ids_mode == "grouped":
+            _, seg, ids, _ = self.sg.group_rows(self.row_ids, self.w.num_adapters, out=self.built)
+        self.sg.lora_apply(s["y"], s["x"], s["A"], s["B"], seg, ids, self.w.scale,
                            workspace=self.workspace)
 
     def reset_outputs(self):
@@ -104,11 +124,11 @@ class BenchState:
         return g
 
 
-def run_gpu(w, steps: int, warmup: int, device="cuda:0"):
+def run_gpu(w, steps: int, warmup: int, device="cuda:0", row_ids=None):
     import torch
     per_set = (w.x.size + w.A.size + w.B.size + w.y0.size) * w.elem_bytes
     nsets = max(1, min(512, math.ceil(ROTATE_BYTES / max(per_set, 1))))
-    st = BenchState(w, nsets, device)
+    st = BenchState(w, nsets, device, row_ids)
     for i in range(warmup):
         st.step(i)
     torch.cuda.synchronize(device)
@@ -217,6 +237,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain BYTES-sized device copy (counter calibration)")
+    ap.add_argument("--row-ids", choices=("runs", "grouped"), default=None,
+                    help="start every step from per-row adapter ids: build the segment "
+                         "table on the device (run table or grouped table), then lora_apply")
     ap.add_argument("--workload", default="llama7b_decode", choices=sorted(WORKLOADS),
                     help="workload to time (default: the Llama-2-7B decode projection); the "
                          "others are the remaining seeded configurations")
@@ -238,7 +261,7 @@ def main(argv=None):
         return 1
 
     w = WORKLOADS[args.workload](wl)
-    res = run_gpu(w, args.steps, args.warmup)
+    res = run_gpu(w, args.steps, args.warmup, row_ids=args.row_ids)
     step_s = res["gpu_ms"] / 1e3 / args.steps
     rows = int(w.seg_lengths.sum())
     abytes = algorithmic_bytes(w)
@@ -261,19 +284,22 @@ def main(argv=None):
             "workload": w.name, "H1": w.H1, "H2": w.H2, "r": w.r, "rows": rows,
             "segments": w.num_segments, "adapters_in_stack": w.num_adapters, "scale": w.scale,
             "buffer_sets_rotated": res["nsets"], "launch": "hip graph of all timed steps",
+            "segment_table": ("given" if args.row_ids is None
+                              else f"built on the device from per-row ids ({args.row_ids})"),
         },
         "us_per_call": step_s * 1e6,
         "achieved_hbm_GBps": achieved,
         "hbm_peak_frac": achieved / HBM_PEAK_GBPS,
         "roofline": {
             "bound": "hbm",
-            "kernel": ("lora_fused_kernel (one launch per step)" if args.workload == "llama7b_decode"
-                       else "every launch of one lora_apply call"),
+            "kernel": ("lora_fused_kernel (one launch per step)"
+                       if args.workload == "llama7b_decode" and args.row_ids is None
+                       else "every launch of one step"),
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": measured_traffic(w.name),
+            "traffic": measured_traffic(w.name) if args.row_ids is None else None,
             "algorithmic_bytes_per_launch": abytes,
             "tflops": flops / step_s / 1e12,
         },

@@ -262,19 +262,33 @@ def validate_segments(seg_indptr, adapter_ids, num_rows, num_adapters) -> int:
                                             ids.shape[0], num_rows, num_adapters))
 
 
-def build_segments(row_ids, num_adapters: int):
+def _outputs(out, sizes, dev, names):
+    """Caller-provided int32 output tensors (checked) or new ones."""
+    torch = _torch()
+    if out is None:
+        return [torch.empty(n, dtype=torch.int32, device=dev) for n in sizes]
+    if len(out) != len(sizes):
+        raise ValueError(f"out must hold {len(sizes)} tensors: {', '.join(names)}")
+    for t, n, name in zip(out, sizes, names):
+        _need(t, name, dev, torch.int32, 1)
+        if t.numel() != n:
+            raise ValueError(f"{name} must have {n} entries, got {t.numel()}")
+    return list(out)
+
+
+def build_segments(row_ids, num_adapters: int, out=None):
     """Segment table from per-row adapter ids (int32 device tensor), one
     segment per maximal run of equal ids.  Returns ``(seg_indptr,
     adapter_ids, num_segments)``: tables of ``num_rows + 1`` / ``num_rows``
     entries whose tail describes empty segments (so they can go straight to
-    ``lora_apply``) and a one-element device tensor with the real count."""
+    ``lora_apply``) and a one-element device tensor with the real count.
+    ``out`` may supply those three tensors."""
     torch = _torch()
     dev = row_ids.device
     _need(row_ids, "row_ids", dev, torch.int32, 1)
     R = row_ids.numel()
-    seg = torch.empty(R + 1, dtype=torch.int32, device=dev)
-    ids = torch.empty(R, dtype=torch.int32, device=dev)
-    count = torch.empty(1, dtype=torch.int32, device=dev)
+    seg, ids, count = _outputs(out, (R + 1, R, 1), dev,
+                               ("seg_indptr", "adapter_ids", "num_segments"))
     _check(lib().sgmv_build_segments(row_ids.data_ptr() if R else None, R, int(num_adapters),
                                      seg.data_ptr(), ids.data_ptr() if R else None,
                                      count.data_ptr(), _stream_ptr(dev)),
@@ -282,21 +296,20 @@ def build_segments(row_ids, num_adapters: int):
     return seg, ids, count
 
 
-def group_rows(row_ids, num_adapters: int):
+def group_rows(row_ids, num_adapters: int, out=None):
     """Stable grouping of rows by adapter (int32 device tensor of per-row
     ids).  Returns ``(perm, seg_indptr, adapter_ids, num_segments)``: row j
     of the grouped batch is row ``perm[j]``; the table describes the grouped
     batch with one segment per adapter present, padded with empty segments
-    to min(num_rows, num_adapters) entries."""
+    to min(num_rows, num_adapters) entries.  ``out`` may supply those four
+    tensors."""
     torch = _torch()
     dev = row_ids.device
     _need(row_ids, "row_ids", dev, torch.int32, 1)
     R = row_ids.numel()
     M = min(R, max(int(num_adapters), 0))
-    perm = torch.empty(R, dtype=torch.int32, device=dev)
-    seg = torch.empty(M + 1, dtype=torch.int32, device=dev)
-    ids = torch.empty(M, dtype=torch.int32, device=dev)
-    count = torch.empty(1, dtype=torch.int32, device=dev)
+    perm, seg, ids, count = _outputs(out, (R, M + 1, M, 1), dev,
+                                     ("perm", "seg_indptr", "adapter_ids", "num_segments"))
     _check(lib().sgmv_group_rows(row_ids.data_ptr() if R else None, R, int(num_adapters),
                                  perm.data_ptr() if R else None, seg.data_ptr(),
                                  ids.data_ptr() if M else None, count.data_ptr(),

@@ -68,6 +68,30 @@ __global__ __launch_bounds__(kSegThreads) void build_segments_kernel(
     if (tid == 0) *num_segments = running;
 }
 
+// Lanes of a wave that share a bin: for a lane with b >= 0, `rank` is the
+// number of lower lanes with the same bin, `cnt` the number of lanes with
+// it, and `last` marks the highest such lane.  One round per distinct bin in
+// the wave (the loop is wave-uniform).
+__device__ __forceinline__ void wave_match(int b, int& rank, int& cnt, bool& last) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const unsigned long long below = (1ull << lane) - 1ull;
+    unsigned long long remaining = __ballot(b >= 0);
+    rank = 0;
+    cnt = 0;
+    last = false;
+    while (remaining) {
+        const int leader = __ffsll((long long)remaining) - 1;
+        const int bl = __shfl(b, leader);
+        const unsigned long long m = __ballot(b == bl);
+        if (b == bl) {
+            rank = __popcll(m & below);
+            cnt = __popcll(m);
+            last = (63 - __clzll((long long)m)) == lane;
+        }
+        remaining &= ~m;
+    }
+}
+
 // Stable grouping.  Bin a < num_adapters holds adapter a's rows, bin
 // num_adapters the rows without a valid adapter.
 __global__ __launch_bounds__(kSegThreads) void group_rows_kernel(
@@ -75,7 +99,6 @@ __global__ __launch_bounds__(kSegThreads) void group_rows_kernel(
     int* __restrict__ seg_indptr, int* __restrict__ adapter_ids, int* __restrict__ num_segments) {
     __shared__ int s_off[kGroupMaxAdapters + 1];  // counts, then first position of each bin
     __shared__ int s_run[kGroupMaxAdapters + 1];  // rows of each bin placed so far
-    __shared__ int s_bin[kSegThreads];
     __shared__ int s_scan[kSegThreads / kWave];
     const int tid = threadIdx.x;
     const int nbins = num_adapters + 1;
@@ -89,7 +112,16 @@ __global__ __launch_bounds__(kSegThreads) void group_rows_kernel(
         s_run[a] = 0;
     }
     __syncthreads();
-    for (int i = tid; i < num_rows; i += kSegThreads) atomicAdd(&s_off[bin_of(i)], 1);
+    // Counts: one LDS addition per bin per wave, so that long runs of one
+    // adapter do not serialise on a single counter.
+    for (int base = 0; base < num_rows; base += kSegThreads) {
+        const int i = base + tid;
+        const int b = i < num_rows ? bin_of(i) : -1;
+        int rank, cnt;
+        bool last;
+        wave_match(b, rank, cnt, last);
+        if (last) atomicAdd(&s_off[b], cnt);
+    }
     __syncthreads();
 
     // Counts -> first positions; adapters present -> segments.
@@ -118,21 +150,26 @@ __global__ __launch_bounds__(kSegThreads) void group_rows_kernel(
     }
     if (tid == 0) *num_segments = segs;
 
-    // Rows in order, a pass of kSegThreads at a time: a row's place in its
-    // bin is the rows of its bin in earlier passes plus those before it in
-    // this pass.
+    // Rows in order, a pass of kSegThreads at a time.  A row's place in its
+    // bin is the bin's rows in earlier passes and earlier waves (s_run) plus
+    // the lower lanes of its wave with the same bin; the waves of a pass take
+    // their turn in order, so the grouping is stable.
+    const int wid = tid / kWave;
     for (int base = 0; base < num_rows; base += kSegThreads) {
         const int i = base + tid;
         const int b = i < num_rows ? bin_of(i) : -1;
-        s_bin[tid] = b;
-        __syncthreads();
-        const int n = min(kSegThreads, num_rows - base);
-        int rank = 0;
-        for (int j = 0; j < n; ++j) rank += (j < tid && s_bin[j] == b) ? 1 : 0;
-        if (b >= 0) perm[s_off[b] + s_run[b] + rank] = i;
-        __syncthreads();
-        if (b >= 0) atomicAdd(&s_run[b], 1);
-        __syncthreads();
+        int rank, cnt;
+        bool last;
+        wave_match(b, rank, cnt, last);
+        for (int w = 0; w < kSegThreads / kWave; ++w) {
+            if (wid == w && b >= 0) {
+                perm[s_off[b] + s_run[b] + rank] = i;
+                // every lane has read s_run[b] before its bin's last lane adds
+                __builtin_amdgcn_wave_barrier();
+                if (last) s_run[b] += cnt;
+            }
+            __syncthreads();
+        }
     }
 }
 
