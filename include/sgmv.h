@@ -160,6 +160,46 @@ int lora_apply(void* y, const void* x, const void* A_stack, const void* B_stack,
                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Several LoRA add-ons over one batch -- e.g. the q, k, v and o projections
+ * of a decoder layer -- in one call: for every problem p,
+ *   problems[p].y[i, :] = round(y + scale_p * (x_p[i, :] @ A_p[a]) @ B_p[a])
+ * with the shared segment table, num_rows, num_adapters, r and dtype, and
+ * each problem's own arrays, H1, H2 and scale.  This amortises the launch
+ * and the shrink-to-expand hand-off, which dominate a decode-sized call
+ * (the pages stress kernel-launch overhead: Punica walkthrough,
+ * omica.com.cn/news/959180, section 2.2).  Results equal those of one
+ * lora_apply per problem.
+ *
+ * problems: HOST array of num_problems (1..SGMV_MAX_PROBLEMS) descriptors;
+ * the pointers in them are device pointers, as for lora_apply, and the
+ * problems must not overlap each other's y.  Decode-shaped calls (vector
+ * ranks, aligned pointers, at most 1024 segments, segments of few rows) run
+ * as one launch; any other call runs as one lora_apply per problem, in order.
+ *
+ * workspace: at least lora_apply_multi_workspace_bytes(...) bytes, with the
+ * conventions of "Workspace" above.  Returns as lora_apply.
+ */
+#define SGMV_MAX_PROBLEMS 8
+typedef struct {
+    void* y;               /* [num_rows, H2], updated in place */
+    const void* x;         /* [num_rows, H1] */
+    const void* A_stack;   /* [num_adapters, H1, r] */
+    const void* B_stack;   /* [num_adapters, r, H2] */
+    int32_t H1;
+    int32_t H2;
+    float scale;
+} sgmv_lora_problem;
+
+size_t lora_apply_multi_workspace_bytes(const sgmv_lora_problem* problems,
+                                        int32_t num_problems, int32_t num_rows,
+                                        int32_t num_segments, int32_t r, int32_t dtype);
+int lora_apply_multi(const sgmv_lora_problem* problems, int32_t num_problems,
+                     const int32_t* seg_indptr, const int32_t* adapter_ids,
+                     int32_t num_segments, int32_t num_rows, int32_t num_adapters,
+                     int32_t r, int32_t dtype, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/*
  * Process-wide patience, in seconds (0 <= seconds <= 10; default 0.02), of
  * the single-kernel lora_apply's expand workgroups waiting for their shrink
  * workgroups.  A workgroup that stops waiting computes its input itself with

@@ -34,6 +34,16 @@ STATUS = {
     4: "SGMV_ERR_UNSUPPORTED", 5: "SGMV_ERR_WORKSPACE", 6: "SGMV_ERR_HIP",
     7: "SGMV_ERR_BAD_SEGMENTS",
 }
+SGMV_MAX_PROBLEMS = 8
+
+
+class LoraProblem(ctypes.Structure):
+    """sgmv_lora_problem of sgmv.h: one add-on of a lora_apply_multi call."""
+    _fields_ = [("y", ctypes.c_void_p), ("x", ctypes.c_void_p), ("A_stack", ctypes.c_void_p),
+                ("B_stack", ctypes.c_void_p), ("H1", ctypes.c_int32), ("H2", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
+
+
 # (name, restype, argtypes) of every symbol the header declares.
 _i32, _sz, _vp, _f32 = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
 ABI = [
@@ -52,6 +62,9 @@ ABI = [
     ("sgmv_validate_segments", ctypes.c_int, [_vp, _vp, _i32, _i32, _i32]),
     ("sgmv_build_segments", ctypes.c_int, [_vp, _i32, _i32, _vp, _vp, _vp, _vp]),
     ("sgmv_group_rows", ctypes.c_int, [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
+    ("lora_apply_multi_workspace_bytes", _sz, [_vp, _i32, _i32, _i32, _i32, _i32]),
+    ("lora_apply_multi", ctypes.c_int, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp,
+                                        _sz, _vp]),
 ]
 
 
@@ -246,6 +259,48 @@ def lora_apply(y, x, A_stack, B_stack, seg_indptr, adapter_ids, scale=1.0, works
     return y
 
 
+def lora_apply_multi(problems, seg_indptr, adapter_ids, workspace=None):
+    """Several add-ons over one batch in one call: ``problems`` is a list of
+    ``(y, x, A_stack, B_stack, scale)`` (each y updated in place, as by
+    ``lora_apply``); all share the segment table, rows, adapter count, rank
+    and dtype.  Returns the list of y tensors."""
+    torch = _torch()
+    problems = list(problems)
+    if not 1 <= len(problems) <= SGMV_MAX_PROBLEMS:
+        raise ValueError(f"between 1 and {SGMV_MAX_PROBLEMS} problems, got {len(problems)}")
+    y0, x0, A0, _, _ = problems[0]
+    dev = x0.device
+    R = x0.shape[0]
+    N, _, r = A0.shape
+    dt = dtype_code(x0.dtype)
+    S = _segments(seg_indptr, adapter_ids, dev)
+    arr = (LoraProblem * len(problems))()
+    for k, (y, x, A_stack, B_stack, scale) in enumerate(problems):
+        _need(x, "x", dev, x0.dtype, 2)
+        _need(y, "y", dev, x0.dtype, 2)
+        _need(A_stack, "A_stack", dev, x0.dtype, 3)
+        _need(B_stack, "B_stack", dev, x0.dtype, 3)
+        H1, H2 = x.shape[1], y.shape[1]
+        if (x.shape[0] != R or y.shape[0] != R or tuple(A_stack.shape) != (N, H1, r)
+                or tuple(B_stack.shape) != (N, r, H2)):
+            raise ValueError(f"problem {k}: shapes disagree (x {tuple(x.shape)}, y {tuple(y.shape)}, "
+                             f"A {tuple(A_stack.shape)}, B {tuple(B_stack.shape)})")
+        arr[k] = LoraProblem(y.data_ptr(), x.data_ptr(), A_stack.data_ptr(), B_stack.data_ptr(),
+                             H1, H2, float(scale))
+    stream = _stream_ptr(dev)
+    parr = ctypes.cast(arr, ctypes.c_void_p)
+    need = int(lib().lora_apply_multi_workspace_bytes(parr, len(problems), R, S, r, dt))
+    if need == 0:
+        raise SGMVError(4, "lora_apply_multi_workspace_bytes")
+    if workspace is None:
+        workspace = _workspaces.get(dev, stream, need)
+    _check(lib().lora_apply_multi(parr, len(problems), seg_indptr.data_ptr(),
+                                  adapter_ids.data_ptr(), S, R, N, r, dt, workspace.data_ptr(),
+                                  workspace.numel() * workspace.element_size(), stream),
+           "lora_apply_multi")
+    return [pr[0] for pr in problems]
+
+
 def set_fused_wait(seconds: float) -> None:
     """Patience of the single-kernel lora_apply's expand workgroups (see sgmv.h)."""
     _check(lib().sgmv_set_fused_wait(float(seconds)), "sgmv_set_fused_wait")
@@ -319,7 +374,7 @@ def group_rows(row_ids, num_adapters: int, out=None):
 
 
 __all__ = [
-    "build_segments", "group_rows",
+    "build_segments", "group_rows", "lora_apply_multi", "LoraProblem",
     "lora_apply", "sgmv_shrink", "sgmv_expand", "lora_apply_workspace_bytes",
     "shrink_workspace_bytes", "validate_segments", "set_fused_wait", "lib", "SGMVError", "ABI", "LIBRARY",
 ]

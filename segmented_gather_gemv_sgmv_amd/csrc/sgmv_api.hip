@@ -118,7 +118,8 @@ struct FusedPlan {
     long long grid;
 };
 
-FusedPlan make_fused_plan(int num_rows, int num_segments, int H1, int H2, int r, int dtype) {
+FusedPlan make_fused_plan(int num_rows, int num_segments, int H1, int H2, int r, int dtype,
+                          long long items = kFusedItems) {
     FusedPlan f{};
     if (!vec_rank(dtype, r)) return f;
     const int vec = vec_width(dtype);
@@ -143,7 +144,7 @@ FusedPlan make_fused_plan(int num_rows, int num_segments, int H1, int H2, int r,
     long long lo = 1;
     while (lo * kFusedMaxChunk < a_bytes && lo < hi) lo *= 2;
     long long k = 1;
-    while (k * 2 <= hi && slots * (k * 2 + f.csplit) <= kFusedItems) k *= 2;
+    while (k * 2 <= hi && slots * (k * 2 + f.csplit) <= items) k *= 2;
     if (k < lo) k = lo;
     const int unit = kFusedThreads / (r / vec);
     long long hps = (H1 + k - 1) / k;
@@ -636,6 +637,171 @@ int lora_apply(void* y, const void* x, const void* A_stack, const void* B_stack,
         using DT = decltype(dt);
         dispatch_expand<DT>(y, part, stride, p.ksplit, B_stack, seg_indptr, adapter_ids,
                             num_segments, num_rows, num_adapters, r, H2, scale, p, st);
+    });
+    return launch_status();
+}
+
+// -- several add-ons in one launch ------------------------------------------
+
+static_assert(kMaxProblems == SGMV_MAX_PROBLEMS, "problem limit mismatch");
+static_assert(sizeof(sgmv_lora_problem) == 48, "sgmv_lora_problem layout");
+
+namespace {
+
+// Plans of the problems of one lora_apply_multi call, or ok = false when the
+// single-launch form does not apply (then each problem runs on its own).
+struct MultiPlan {
+    bool ok;
+    FusedPlan f[kMaxProblems];
+    size_t partial_off[kMaxProblems + 1];  // in floats, after the counter region
+};
+
+MultiPlan make_multi_plan(const sgmv_lora_problem* pr, int P, int num_rows, int num_segments,
+                          int r, int dtype) {
+    MultiPlan m{};
+    if (P < 1 || P > kMaxProblems || num_segments > kCompactMaxSegments) return m;
+    const long long budget = kFusedItems / P > 64 ? kFusedItems / P : 64;
+    long long slots_total = 0;
+    m.partial_off[0] = 0;
+    for (int p = 0; p < P; ++p) {
+        m.f[p] = make_fused_plan(num_rows, num_segments, pr[p].H1, pr[p].H2, r, dtype, budget);
+        if (!m.f[p].ok || m.f[p].rows != m.f[0].rows) return m;
+        slots_total += m.f[p].slots_a;
+        m.partial_off[p + 1] =
+            m.partial_off[p] + (size_t)m.f[p].ksplit * (size_t)num_rows * (size_t)r;
+    }
+    long long items = 0;
+    for (int p = 0; p < P; ++p) items += m.f[p].grid;
+    m.ok = slots_total <= kCounterSlots && items <= kMaxGrid;
+    return m;
+}
+
+bool problem_fits_fused(const sgmv_lora_problem& q, int dtype) {
+    return aligned16(q.A_stack) && aligned16(q.B_stack) && aligned16(q.y) &&
+           q.H2 % vec_width(dtype) == 0;
+}
+
+}  // namespace
+
+size_t lora_apply_multi_workspace_bytes(const sgmv_lora_problem* problems, int32_t num_problems,
+                                        int32_t num_rows, int32_t num_segments, int32_t r,
+                                        int32_t dtype) {
+    if (!problems || num_problems < 1 || num_problems > SGMV_MAX_PROBLEMS) return 0;
+    if (check_common(num_segments, num_rows, 0, r, dtype) != SGMV_OK) return 0;
+    size_t need = 0;
+    for (int p = 0; p < num_problems; ++p) {
+        const size_t one = lora_apply_workspace_bytes(num_rows, num_segments, problems[p].H1,
+                                                      problems[p].H2, r, dtype);
+        if (one == 0) return 0;
+        if (one > need) need = one;
+    }
+    const MultiPlan m = make_multi_plan(problems, num_problems, num_rows, num_segments, r, dtype);
+    if (m.ok) {
+        const size_t multi = kCounterBytes + m.partial_off[num_problems] * sizeof(float);
+        if (multi > need) need = multi;
+    }
+    return need;
+}
+
+int lora_apply_multi(const sgmv_lora_problem* problems, int32_t num_problems,
+                     const int32_t* seg_indptr, const int32_t* adapter_ids, int32_t num_segments,
+                     int32_t num_rows, int32_t num_adapters, int32_t r, int32_t dtype,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+    if (!problems) return SGMV_ERR_NULL_PTR;
+    if (num_problems < 1 || num_problems > SGMV_MAX_PROBLEMS) return SGMV_ERR_BAD_SHAPE;
+    int rc = check_common(num_segments, num_rows, num_adapters, r, dtype);
+    if (rc != SGMV_OK) return rc;
+    for (int p = 0; p < num_problems; ++p) {
+        const sgmv_lora_problem& q = problems[p];
+        if (q.H1 < 1 || q.H2 < 1) return SGMV_ERR_BAD_SHAPE;
+        if (num_rows > 0 && num_segments > 0 && (!q.y || !q.x || !q.A_stack || !q.B_stack))
+            return SGMV_ERR_NULL_PTR;
+    }
+    if (num_rows == 0 || num_segments == 0) return SGMV_OK;
+    if (!seg_indptr || !adapter_ids) return SGMV_ERR_NULL_PTR;
+    const size_t need = lora_apply_multi_workspace_bytes(problems, num_problems, num_rows,
+                                                         num_segments, r, dtype);
+    if (need == 0) return SGMV_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < need) return SGMV_ERR_WORKSPACE;
+
+    const MultiPlan m = make_multi_plan(problems, num_problems, num_rows, num_segments, r, dtype);
+    bool one_launch = m.ok;
+    for (int p = 0; p < num_problems && one_launch; ++p)
+        one_launch = problem_fits_fused(problems[p], dtype) &&
+                     !use_mfma(num_rows, num_segments);
+    if (!one_launch) {
+        // One call per problem, in order, each with the whole workspace.
+        for (int p = 0; p < num_problems; ++p) {
+            const sgmv_lora_problem& q = problems[p];
+            rc = lora_apply(q.y, q.x, q.A_stack, q.B_stack, seg_indptr, adapter_ids, num_segments,
+                            num_rows, num_adapters, q.H1, q.H2, r, q.scale, dtype, workspace,
+                            workspace_bytes, stream);
+            if (rc != SGMV_OK) return rc;
+        }
+        return SGMV_OK;
+    }
+
+    hipStream_t st = (hipStream_t)stream;
+    int* counters = (int*)workspace;
+    float* part = (float*)((char*)workspace + kCounterBytes);
+    const double wait_s = fused_wait_seconds();
+    const long long wait =
+        wait_s < 1e-300 ? -1 : (long long)(wait_s * (double)wall_ticks_per_second());
+    const FusedPlan& f0 = m.f[0];
+    with_dtype(dtype, [&](auto dt) {
+        using DT = decltype(dt);
+        using T = typename DT::storage;
+        MultiProblems<T> P{};
+        P.num = num_problems;
+        long long next_counter = 0, next_item = 0;
+        for (int p = 0; p < num_problems; ++p) {
+            const sgmv_lora_problem& q = problems[p];
+            const FusedPlan& f = m.f[p];
+            P.y[p] = (T*)q.y;
+            P.x[p] = (const T*)q.x;
+            P.A[p] = (const T*)q.A_stack;
+            P.B[p] = (const T*)q.B_stack;
+            P.partials[p] = part + m.partial_off[p];
+            P.counters[p] = counters + next_counter * kCounterStride;
+            next_counter += f.slots_a;
+            P.H1[p] = q.H1;
+            P.H2[p] = q.H2;
+            P.ksplit[p] = f.ksplit;
+            P.h_per_split[p] = f.h_per_split;
+            P.csplit[p] = f.csplit;
+            P.scale[p] = q.scale;
+            P.sbase[p] = next_item;
+            next_item += f.slots_a * f.ksplit;
+        }
+        P.sbase[num_problems] = next_item;
+        for (int p = 0; p < num_problems; ++p) {
+            P.ebase[p] = next_item;
+            next_item += m.f[p].slots_a * m.f[p].csplit;
+        }
+        P.ebase[num_problems] = next_item;
+        auto go = [&](auto rank, auto rows) {
+            constexpr int R = decltype(rank)::value;
+            constexpr int RB = decltype(rows)::value;
+            constexpr int KB = R < 16 ? R : 16;
+            launch(&lora_fused_multi_kernel<DT, R, kFusedThreads, RB, kFusedPG, KB>,
+                   dim3((unsigned)next_item), dim3(kFusedThreads), st, P, seg_indptr,
+                   adapter_ids, num_segments, num_rows, num_adapters, f0.compact,
+                   &counters[kCounterInts - 1], kCounterStride, wait);
+        };
+        auto by_rows = [&](auto rank) {
+            if (f0.rows == 1) go(rank, std::integral_constant<int, 1>{});
+            else go(rank, std::integral_constant<int, 4>{});
+        };
+        switch (r) {
+            case 4:
+                if constexpr (DT::kVec == 4) by_rows(std::integral_constant<int, 4>{});
+                break;
+            case 8: by_rows(std::integral_constant<int, 8>{}); break;
+            case 16: by_rows(std::integral_constant<int, 16>{}); break;
+            case 32: by_rows(std::integral_constant<int, 32>{}); break;
+            case 64: by_rows(std::integral_constant<int, 64>{}); break;
+            default: by_rows(std::integral_constant<int, 128>{}); break;
+        }
     });
     return launch_status();
 }

@@ -226,15 +226,18 @@ __device__ __forceinline__ Item decode_item(int slots_a, int slots_b, int ksplit
     return it;
 }
 
+// One item of the single-kernel lora_apply: the shrink of H1 chunk `sub`
+// (is_shrink) or the expand of column chunk `sub` of tile slot g.  `counters`
+// holds the tile counters of this problem; `flag` is the sticky flag.
 template <typename DT, int R, int NT, int RB, int PG, int KB>
-__global__ __launch_bounds__(NT) void lora_fused_kernel(
-    typename DT::storage* __restrict__ y, const typename DT::storage* __restrict__ x,
-    const typename DT::storage* __restrict__ A_stack,
+__device__ __forceinline__ void fused_item(
+    bool is_shrink, int g, int sub, typename DT::storage* __restrict__ y,
+    const typename DT::storage* __restrict__ x, const typename DT::storage* __restrict__ A_stack,
     const typename DT::storage* __restrict__ B_stack, const int* __restrict__ seg_indptr,
     const int* __restrict__ adapter_ids, int S, int num_rows, int num_adapters, int H1, int H2,
     float scale, float* __restrict__ partials, int* __restrict__ counters, int ksplit,
-    int h_per_split, int csplit, int slots_a, int slots_b, int compact, int n_counters,
-    int counter_stride, long long wait_ticks) {
+    int h_per_split, int csplit, int compact, int* flag, int counter_stride,
+    long long wait_ticks) {
     using st = typename DT::storage;
     constexpr int VEC = DT::kVec;
     constexpr int CW = NT * VEC;  // columns per expand item
@@ -251,7 +254,6 @@ __global__ __launch_bounds__(NT) void lora_fused_kernel(
     const int tid = threadIdx.x;
     const long long row_stride = (long long)num_rows * R;  // between chunk partials
 
-    const Item it = decode_item(slots_a, slots_b, ksplit, csplit);
     auto locate = [&](int g, Tile& t) {
         return compact ? locate_tile_compact<NT>(seg_indptr, adapter_ids, S, num_rows,
                                                  num_adapters, RB, g, s_scan, t)
@@ -259,10 +261,9 @@ __global__ __launch_bounds__(NT) void lora_fused_kernel(
                                          RB, g, s_scan, t);
     };
 
-    if (it.shrink) {
+    if (is_shrink) {
         // ---------------- shrink item ----------------
-        const int g = it.g;
-        const int p = it.sub;
+        const int p = sub;
         Tile tile;
         if (locate(g, tile)) {
             const int h_lo = p * h_per_split;
@@ -282,8 +283,7 @@ __global__ __launch_bounds__(NT) void lora_fused_kernel(
         }
     } else {
         // ---------------- expand item ----------------
-        const int g = it.g;
-        const int c = it.sub;
+        const int c = sub;
         Tile tile;
         if (locate(g, tile)) {
             const int nrows = tile.nrows;
@@ -325,8 +325,7 @@ __global__ __launch_bounds__(NT) void lora_fused_kernel(
             } else {
                 // The producers are late: compute every chunk here, summing in
                 // the same order as the normal path.
-                if (tid == 0) __hip_atomic_store(&counters[n_counters - 1], 1, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
+                if (tid == 0) __hip_atomic_store(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 for (int t = tid; t < RB * R; t += NT) s_v[t] = 0.f;
                 __syncthreads();
                 const st* A = A_stack + (long long)tile.adapter * H1 * R;
@@ -399,6 +398,71 @@ __global__ __launch_bounds__(NT) void lora_fused_kernel(
     }
 
     // ---------------- completion: the last workgroup resets the counters ----
+}
+
+template <typename DT, int R, int NT, int RB, int PG, int KB>
+__global__ __launch_bounds__(NT) void lora_fused_kernel(
+    typename DT::storage* __restrict__ y, const typename DT::storage* __restrict__ x,
+    const typename DT::storage* __restrict__ A_stack,
+    const typename DT::storage* __restrict__ B_stack, const int* __restrict__ seg_indptr,
+    const int* __restrict__ adapter_ids, int S, int num_rows, int num_adapters, int H1, int H2,
+    float scale, float* __restrict__ partials, int* __restrict__ counters, int ksplit,
+    int h_per_split, int csplit, int slots_a, int slots_b, int compact, int n_counters,
+    int counter_stride, long long wait_ticks) {
+    const Item it = decode_item(slots_a, slots_b, ksplit, csplit);
+    fused_item<DT, R, NT, RB, PG, KB>(it.shrink, it.g, it.sub, y, x, A_stack, B_stack, seg_indptr,
+                                      adapter_ids, S, num_rows, num_adapters, H1, H2, scale,
+                                      partials, counters, ksplit, h_per_split, csplit, compact,
+                                      &counters[n_counters - 1], counter_stride, wait_ticks);
+}
+
+// ---------------------------------------------------------------------------
+// Several add-ons over one batch in one launch (e.g. the LoRA projections of
+// a layer): problem p has its own y, x, stacks, H1, H2, scale, plan,
+// partials and tile counters, and all share the segment table.  Workgroups
+// [sbase[p], sbase[p + 1]) are problem p's shrink items and, after every
+// shrink item, [ebase[p], ebase[p + 1]) its expand items, so every wait is on
+// lower-numbered workgroups, as in lora_fused_kernel.  A decode step pays the
+// launch and the hand-off latency once for all its projections instead of
+// once per projection (kernel-launch overhead matters at this scale: Punica
+// walkthrough, omica.com.cn/news/959180, section 2.2).
+// ---------------------------------------------------------------------------
+constexpr int kMaxProblems = 8;
+
+template <typename T>
+struct MultiProblems {
+    T* y[kMaxProblems];
+    const T* x[kMaxProblems];
+    const T* A[kMaxProblems];
+    const T* B[kMaxProblems];
+    float* partials[kMaxProblems];
+    int* counters[kMaxProblems];
+    int H1[kMaxProblems], H2[kMaxProblems];
+    int ksplit[kMaxProblems], h_per_split[kMaxProblems], csplit[kMaxProblems];
+    float scale[kMaxProblems];
+    long long sbase[kMaxProblems + 1];  // shrink items of problem p: [sbase[p], sbase[p + 1])
+    long long ebase[kMaxProblems + 1];  // expand items: [ebase[p], ebase[p + 1]), ebase[0] = sbase[num]
+    int num;
+};
+
+template <typename DT, int R, int NT, int RB, int PG, int KB>
+__global__ __launch_bounds__(NT) void lora_fused_multi_kernel(
+    MultiProblems<typename DT::storage> P, const int* __restrict__ seg_indptr,
+    const int* __restrict__ adapter_ids, int S, int num_rows, int num_adapters, int compact,
+    int* flag, int counter_stride, long long wait_ticks) {
+    const long long b = blockIdx.x;
+    const bool shrink = b < P.sbase[P.num];
+    const long long* base = shrink ? P.sbase : P.ebase;
+    int p = 0;
+    while (p + 1 < P.num && b >= base[p + 1]) ++p;
+    const long long local = b - base[p];
+    const int split = shrink ? P.ksplit[p] : P.csplit[p];
+    fused_item<DT, R, NT, RB, PG, KB>(shrink, (int)(local / split), (int)(local % split), P.y[p],
+                                      P.x[p], P.A[p], P.B[p], seg_indptr, adapter_ids, S,
+                                      num_rows, num_adapters, P.H1[p], P.H2[p], P.scale[p],
+                                      P.partials[p], P.counters[p], P.ksplit[p],
+                                      P.h_per_split[p], P.csplit[p], compact, flag,
+                                      counter_stride, wait_ticks);
 }
 
 }  // namespace sgmv

@@ -143,3 +143,25 @@ def test_set_fused_wait_validates(lib):
 
 def test_last_hip_error_is_readable(lib):
     assert isinstance(lib.sgmv_last_hip_error(), bytes)
+
+
+def test_lora_apply_multi_host_checks(lib):
+    """Argument errors of lora_apply_multi come back before anything is
+    enqueued; the descriptor layout matches the header's."""
+    import ctypes
+    import segmented_gather_gemv_sgmv_amd as sg
+    assert ctypes.sizeof(sg.LoraProblem) == 48
+    arr = (sg.LoraProblem * 2)()
+    p = ctypes.cast(arr, ctypes.c_void_p)
+    assert lib.lora_apply_multi(None, 1, None, None, 1, 1, 1, 16, 1, None, 0, None) == 1
+    assert lib.lora_apply_multi(p, 0, None, None, 1, 1, 1, 16, 1, None, 0, None) == 2
+    assert lib.lora_apply_multi(p, 9, None, None, 1, 1, 1, 16, 1, None, 0, None) == 2
+    for k in range(2):  # H1 = H2 = 0
+        arr[k] = sg.LoraProblem(None, None, None, None, 0, 0, 1.0)
+    assert lib.lora_apply_multi(p, 2, None, None, 1, 1, 1, 16, 1, None, 0, None) == 2
+    for k in range(2):
+        arr[k] = sg.LoraProblem(None, None, None, None, 4096, 4096, 1.0)
+    assert lib.lora_apply_multi(p, 2, None, None, 64, 64, 64, 16, 1, None, 0, None) == 1
+    one = lib.lora_apply_workspace_bytes(64, 64, 4096, 4096, 16, 1)
+    assert lib.lora_apply_multi_workspace_bytes(p, 2, 64, 64, 16, 1) >= one
+    assert lib.lora_apply_multi_workspace_bytes(p, 0, 64, 64, 16, 1) == 0
