@@ -59,7 +59,7 @@ def algorithmic_flops(w) -> int:
 class BenchState:
     """Device copies of a workload, rotated over `nsets` buffer sets."""
 
-    def __init__(self, w, nsets: int, device="cuda:0", row_ids=None):
+    def __init__(self, w, nsets: int, device="cuda:0", row_ids=None, projections=1):
         import torch
         import segmented_gather_gemv_sgmv_amd as sg
         self.w = w
@@ -72,12 +72,21 @@ class BenchState:
         self.seg = torch.from_numpy(w.seg_indptr).to(dev)
         self.ids = torch.from_numpy(w.adapter_ids).to(dev)
         self.sets = []
+        self.projections = projections
         for i in range(nsets):
-            s = {k: (v if i == 0 else v.clone()) for k, v in base.items() if k != "y0"}
-            s["y"] = base["y0"].clone()
+            if projections == 1:
+                s = {k: (v if i == 0 else v.clone()) for k, v in base.items() if k != "y0"}
+                s["y"] = base["y0"].clone()
+            else:  # one copy of the shape per projection
+                s = {k: [v.clone() for _ in range(projections)] for k, v in base.items()
+                     if k != "y0"}
+                s["y"] = [base["y0"].clone() for _ in range(projections)]
             self.sets.append(s)
         self.y0 = base["y0"]
         nbytes = sg.lora_apply_workspace_bytes(w.num_rows, w.num_segments, w.H1, w.H2, w.r, dt)
+        if projections > 1:
+            nbytes = max(nbytes, sg.lora_apply_multi_workspace_bytes(
+                [(w.H1, w.H2)] * projections, w.num_rows, w.num_segments, w.r, dt))
         self.device = dev
         self.row_ids_mode = row_ids
         if row_ids:
@@ -101,12 +110,18 @@ class BenchState:
             seg, ids, _ = self.sg.build_segments(self.row_ids, self.w.num_adapters, out=self.built)
         elif self.row_ids_mode == "grouped":
             _, seg, ids, _ = self.sg.group_rows(self.row_ids, self.w.num_adapters, out=self.built)
+        if self.projections > 1:
+            self.sg.lora_apply_multi(
+                [(s["y"][p], s["x"][p], s["A"][p], s["B"][p], self.w.scale)
+                 for p in range(self.projections)], seg, ids, workspace=self.workspace)
+            return
         self.sg.lora_apply(s["y"], s["x"], s["A"], s["B"], seg, ids, self.w.scale,
                            workspace=self.workspace)
 
     def reset_outputs(self):
         for s in self.sets:
-            s["y"].copy_(self.y0)
+            for y in (s["y"] if isinstance(s["y"], list) else [s["y"]]):
+                y.copy_(self.y0)
 
     def capture(self, nsteps: int, first: int = 0):
         """A HIP graph of `nsteps` consecutive steps starting at set `first`."""
@@ -124,11 +139,11 @@ class BenchState:
         return g
 
 
-def run_gpu(w, steps: int, warmup: int, device="cuda:0", row_ids=None):
+def run_gpu(w, steps: int, warmup: int, device="cuda:0", row_ids=None, projections=1):
     import torch
-    per_set = (w.x.size + w.A.size + w.B.size + w.y0.size) * w.elem_bytes
+    per_set = (w.x.size + w.A.size + w.B.size + w.y0.size) * w.elem_bytes * projections
     nsets = max(1, min(512, math.ceil(ROTATE_BYTES / max(per_set, 1))))
-    st = BenchState(w, nsets, device, row_ids)
+    st = BenchState(w, nsets, device, row_ids, projections)
     for i in range(warmup):
         st.step(i)
     torch.cuda.synchronize(device)
@@ -240,6 +255,9 @@ def main(argv=None):
     ap.add_argument("--row-ids", choices=("runs", "grouped"), default=None,
                     help="start every step from per-row adapter ids: build the segment "
                          "table on the device (run table or grouped table), then lora_apply")
+    ap.add_argument("--projections", type=int, default=1, choices=range(1, 9), metavar="P",
+                    help="P add-ons of the workload's shape over the same batch in one "
+                         "lora_apply_multi call (e.g. a layer's q/k/v/o projections)")
     ap.add_argument("--workload", default="llama7b_decode", choices=sorted(WORKLOADS),
                     help="workload to time (default: the Llama-2-7B decode projection); the "
                          "others are the remaining seeded configurations")
@@ -261,11 +279,12 @@ def main(argv=None):
         return 1
 
     w = WORKLOADS[args.workload](wl)
-    res = run_gpu(w, args.steps, args.warmup, row_ids=args.row_ids)
+    P = args.projections
+    res = run_gpu(w, args.steps, args.warmup, row_ids=args.row_ids, projections=P)
     step_s = res["gpu_ms"] / 1e3 / args.steps
-    rows = int(w.seg_lengths.sum())
-    abytes = algorithmic_bytes(w)
-    flops = algorithmic_flops(w)
+    rows = int(w.seg_lengths.sum()) * P  # a row through one add-on is one SGMV row
+    abytes = algorithmic_bytes(w) * P
+    flops = algorithmic_flops(w) * P
     achieved = abytes / step_s / 1e9
     line = {
         "metric": "SGMV rows/s and achieved HBM GB/s (% of peak) per layer call, H=4096 r=16",
@@ -284,6 +303,7 @@ def main(argv=None):
             "workload": w.name, "H1": w.H1, "H2": w.H2, "r": w.r, "rows": rows,
             "segments": w.num_segments, "adapters_in_stack": w.num_adapters, "scale": w.scale,
             "buffer_sets_rotated": res["nsets"], "launch": "hip graph of all timed steps",
+            "projections": P,
             "segment_table": ("given" if args.row_ids is None
                               else f"built on the device from per-row ids ({args.row_ids})"),
         },
@@ -293,13 +313,13 @@ def main(argv=None):
         "roofline": {
             "bound": "hbm",
             "kernel": ("lora_fused_kernel (one launch per step)"
-                       if args.workload == "llama7b_decode" and args.row_ids is None
+                       if args.workload == "llama7b_decode" and args.row_ids is None and P == 1
                        else "every launch of one step"),
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": measured_traffic(w.name) if args.row_ids is None else None,
+            "traffic": measured_traffic(w.name) if args.row_ids is None and P == 1 else None,
             "algorithmic_bytes_per_launch": abytes,
             "tflops": flops / step_s / 1e12,
         },

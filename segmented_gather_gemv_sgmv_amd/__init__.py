@@ -259,6 +259,16 @@ def lora_apply(y, x, A_stack, B_stack, seg_indptr, adapter_ids, scale=1.0, works
     return y
 
 
+def lora_apply_multi_workspace_bytes(shapes, num_rows, num_segments, r, dtype) -> int:
+    """Workspace bytes of a lora_apply_multi call whose problems have the
+    given (H1, H2) shapes."""
+    arr = (LoraProblem * len(shapes))(*[LoraProblem(None, None, None, None, int(h1), int(h2), 1.0)
+                                        for h1, h2 in shapes])
+    return int(lib().lora_apply_multi_workspace_bytes(ctypes.cast(arr, ctypes.c_void_p),
+                                                      len(shapes), num_rows, num_segments, r,
+                                                      dtype_code(dtype)))
+
+
 def lora_apply_multi(problems, seg_indptr, adapter_ids, workspace=None):
     """Several add-ons over one batch in one call: ``problems`` is a list of
     ``(y, x, A_stack, B_stack, scale)`` (each y updated in place, as by
@@ -374,7 +384,8 @@ def group_rows(row_ids, num_adapters: int, out=None):
 
 
 __all__ = [
-    "build_segments", "group_rows", "lora_apply_multi", "LoraProblem",
+    "build_segments", "group_rows", "lora_apply_multi", "lora_apply_multi_workspace_bytes",
+    "LoraProblem",
     "lora_apply", "sgmv_shrink", "sgmv_expand", "lora_apply_workspace_bytes",
     "shrink_workspace_bytes", "validate_segments", "set_fused_wait", "lib", "SGMVError", "ABI", "LIBRARY",
 ]

@@ -660,7 +660,10 @@ MultiPlan make_multi_plan(const sgmv_lora_problem* pr, int P, int num_rows, int 
                           int r, int dtype) {
     MultiPlan m{};
     if (P < 1 || P > kMaxProblems || num_segments > kCompactMaxSegments) return m;
-    const long long budget = kFusedItems / P > 64 ? kFusedItems / P : 64;
+    // Two resident rounds of items in all: smaller items per problem than one
+    // round would allow, whose loads are in flight together (measured best
+    // for 2 and 4 decode projections; equal for 8).
+    const long long budget = 2 * kFusedItems / P > 64 ? 2 * kFusedItems / P : 64;
     long long slots_total = 0;
     m.partial_off[0] = 0;
     for (int p = 0; p < P; ++p) {
