@@ -223,6 +223,58 @@ def cpu_baseline(w, budget_s: float = 10.0):
                        f"({el:.1f} s, one thread)")
 
 
+def adapter_load(w, reps: int = 20, device="cuda:0"):
+    """On-demand loading: the workload's whole adapter stack copied from
+    pinned host memory (the cold start of one layer's stack) in one call and
+    with one call per adapter, and one adapter alone; HIP events around
+    `reps` repetitions each."""
+    import torch
+    import segmented_gather_gemv_sgmv_amd as sg
+    dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    dev = torch.device(device)
+    hA = torch.empty(w.A.shape, dtype=dt, pin_memory=True)
+    hB = torch.empty(w.B.shape, dtype=dt, pin_memory=True)
+    hA.copy_(torch.from_numpy(w.A).to(dt))
+    hB.copy_(torch.from_numpy(w.B).to(dt))
+    A_dev = torch.empty(w.A.shape, dtype=dt, device=dev)
+    B_dev = torch.empty(w.B.shape, dtype=dt, device=dev)
+    N = w.num_adapters
+
+    def load(slots):
+        if slots == "all":  # the whole stack in one call: two copies
+            sg.load_adapter(A_dev, B_dev, 0, hA, hB)
+            return
+        for k in slots:
+            sg.load_adapter(A_dev, B_dev, k, hA[k], hB[k])
+
+    def timed(slots):
+        load(slots)
+        torch.cuda.synchronize(dev)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            load(slots)
+        b.record()
+        torch.cuda.synchronize(dev)
+        return a.elapsed_time(b) / 1e3 / reps
+
+    per_adapter = (w.H1 * w.r + w.r * w.H2) * w.elem_bytes
+    t_all = timed("all")
+    t_each = timed(range(N))
+    t_one = timed([0])
+    ok = torch.equal(A_dev.cpu(), hA) and torch.equal(B_dev.cpu(), hB)
+    return {
+        "metric": "on-demand adapter load, host (pinned) to device stack",
+        "value": N * per_adapter / t_all / 1e9, "unit": "GB/s", "higher_is_better": True,
+        "n_gpus": 1, "data": "synthetic (seeded)",
+        "config": {"workload": w.name, "adapters": N, "bytes_per_adapter": per_adapter,
+                   "repetitions": reps},
+        "us_whole_stack": t_all * 1e6, "us_whole_stack_one_call_per_adapter": t_each * 1e6,
+        "us_one_adapter": t_one * 1e6, "copied_correctly": ok,
+    }
+
+
 # Timed workloads by name: the decode projection the metric is quoted on, and
 # the other seeded configurations (each a lora_apply call of its own shape).
 WORKLOADS = {
@@ -255,6 +307,9 @@ def main(argv=None):
     ap.add_argument("--row-ids", choices=("runs", "grouped"), default=None,
                     help="start every step from per-row adapter ids: build the segment "
                          "table on the device (run table or grouped table), then lora_apply")
+    ap.add_argument("--adapter-load", action="store_true",
+                    help="instead: time on-demand loading of the workload's adapters from "
+                         "pinned host memory into the device stacks (sgmv_load_adapter)")
     ap.add_argument("--projections", type=int, default=1, choices=range(1, 9), metavar="P",
                     help="P add-ons of the workload's shape over the same batch in one "
                          "lora_apply_multi call (e.g. a layer's q/k/v/o projections)")
@@ -279,6 +334,9 @@ def main(argv=None):
         return 1
 
     w = WORKLOADS[args.workload](wl)
+    if args.adapter_load:
+        print(json.dumps(adapter_load(w)), flush=True)
+        return 0
     P = args.projections
     res = run_gpu(w, args.steps, args.warmup, row_ids=args.row_ids, projections=P)
     step_s = res["gpu_ms"] / 1e3 / args.steps

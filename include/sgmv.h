@@ -200,6 +200,25 @@ int lora_apply_multi(const sgmv_lora_problem* problems, int32_t num_problems,
                      void* stream);
 
 /*
+ * On-demand adapter loading: copies `count` adapters from HOST memory into
+ * slots [slot, slot + count) of the device stacks -- h_A [count, H1, r]
+ * into A_stack[slot ..] and h_B [count, r, H2] into B_stack[slot ..], all
+ * row-major in the stacks' dtype -- with two asynchronous copies on
+ * `stream`, so that the next lora_apply on that stream sees them.  Adapters not yet resident are brought in this way when a
+ * request needs them (Punica review, nubint.ai, "Proposed method": the
+ * system loads LoRA models on demand and keeps only the base model
+ * resident).  For the copy to overlap other work the host buffers must be
+ * pinned (hipHostMalloc); pageable buffers are staged by the runtime.  The
+ * host buffers must stay valid until the copies have completed.  Returns
+ * SGMV_OK, SGMV_ERR_NULL_PTR, SGMV_ERR_BAD_SHAPE (slots outside
+ * [0, num_adapters), count < 1, bad sizes), SGMV_ERR_BAD_DTYPE or
+ * SGMV_ERR_HIP.
+ */
+int sgmv_load_adapter(void* A_stack, void* B_stack, int32_t slot, int32_t count,
+                      int32_t num_adapters, const void* h_A, const void* h_B, int32_t H1,
+                      int32_t H2, int32_t r, int32_t dtype, void* stream);
+
+/*
  * Process-wide patience, in seconds (0 <= seconds <= 10; default 0.02), of
  * the single-kernel lora_apply's expand workgroups waiting for their shrink
  * workgroups.  A workgroup that stops waiting computes its input itself with

@@ -62,6 +62,8 @@ ABI = [
     ("sgmv_validate_segments", ctypes.c_int, [_vp, _vp, _i32, _i32, _i32]),
     ("sgmv_build_segments", ctypes.c_int, [_vp, _i32, _i32, _vp, _vp, _vp, _vp]),
     ("sgmv_group_rows", ctypes.c_int, [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
+    ("sgmv_load_adapter", ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _i32, _i32, _i32,
+                                         _i32, _vp]),
     ("lora_apply_multi_workspace_bytes", _sz, [_vp, _i32, _i32, _i32, _i32, _i32]),
     ("lora_apply_multi", ctypes.c_int, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp,
                                         _sz, _vp]),
@@ -311,6 +313,32 @@ def lora_apply_multi(problems, seg_indptr, adapter_ids, workspace=None):
     return [pr[0] for pr in problems]
 
 
+def load_adapter(A_stack, B_stack, slot: int, A, B):
+    """Copy adapters from host tensors into the device stacks, on the current
+    stream: A [H1, r] and B [r, H2] for one adapter into slot ``slot``, or
+    A [count, H1, r] and B [count, r, H2] into slots [slot, slot + count).
+    Pin the host tensors for an asynchronous copy."""
+    dev = A_stack.device
+    _need(A_stack, "A_stack", dev, None, 3)
+    _need(B_stack, "B_stack", dev, A_stack.dtype, 3)
+    N, H1, r = A_stack.shape
+    H2 = B_stack.shape[2]
+    if A.device.type != "cpu" or B.device.type != "cpu":
+        raise ValueError("A and B must be host tensors")
+    count = 1 if A.dim() == 2 else A.shape[0]
+    if tuple(A.shape[-2:]) != (H1, r) or tuple(B.shape[-2:]) != (r, H2) or \
+            A.dim() not in (2, 3) or B.dim() != A.dim() or (A.dim() == 3 and B.shape[0] != count):
+        raise ValueError(f"A must be [count,] {(H1, r)} and B [count,] {(r, H2)}")
+    if A.dtype != A_stack.dtype or B.dtype != A_stack.dtype:
+        raise TypeError("A and B must have the stacks' dtype")
+    if not A.is_contiguous() or not B.is_contiguous():
+        raise ValueError("A and B must be contiguous")
+    _check(lib().sgmv_load_adapter(A_stack.data_ptr(), B_stack.data_ptr(), int(slot), count, N,
+                                   A.data_ptr(), B.data_ptr(), H1, H2, r,
+                                   dtype_code(A_stack.dtype), _stream_ptr(dev)),
+           "sgmv_load_adapter")
+
+
 def set_fused_wait(seconds: float) -> None:
     """Patience of the single-kernel lora_apply's expand workgroups (see sgmv.h)."""
     _check(lib().sgmv_set_fused_wait(float(seconds)), "sgmv_set_fused_wait")
@@ -385,6 +413,7 @@ def group_rows(row_ids, num_adapters: int, out=None):
 
 __all__ = [
     "build_segments", "group_rows", "lora_apply_multi", "lora_apply_multi_workspace_bytes",
+    "load_adapter",
     "LoraProblem",
     "lora_apply", "sgmv_shrink", "sgmv_expand", "lora_apply_workspace_bytes",
     "shrink_workspace_bytes", "validate_segments", "set_fused_wait", "lib", "SGMVError", "ABI", "LIBRARY",

@@ -809,6 +809,30 @@ int lora_apply_multi(const sgmv_lora_problem* problems, int32_t num_problems,
     return launch_status();
 }
 
+int sgmv_load_adapter(void* A_stack, void* B_stack, int32_t slot, int32_t count,
+                      int32_t num_adapters, const void* h_A, const void* h_B, int32_t H1,
+                      int32_t H2, int32_t r, int32_t dtype, void* stream) {
+    if (dtype != SGMV_F32 && dtype != SGMV_F16 && dtype != SGMV_BF16) return SGMV_ERR_BAD_DTYPE;
+    if (H1 < 1 || H2 < 1 || r < 1 || r > SGMV_MAX_RANK || num_adapters < 1 || slot < 0 ||
+        count < 1 || (long long)slot + count > num_adapters)
+        return SGMV_ERR_BAD_SHAPE;
+    if (!A_stack || !B_stack || !h_A || !h_B) return SGMV_ERR_NULL_PTR;
+    const size_t e = (size_t)elem_bytes(dtype);
+    const size_t a_bytes = (size_t)H1 * (size_t)r * e;  // one adapter
+    const size_t b_bytes = (size_t)r * (size_t)H2 * e;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t err = hipMemcpyAsync((char*)A_stack + (size_t)slot * a_bytes, h_A,
+                                    a_bytes * (size_t)count, hipMemcpyHostToDevice, st);
+    if (err == hipSuccess)
+        err = hipMemcpyAsync((char*)B_stack + (size_t)slot * b_bytes, h_B,
+                             b_bytes * (size_t)count, hipMemcpyHostToDevice, st);
+    if (err != hipSuccess) {
+        t_last = err;
+        return SGMV_ERR_HIP;
+    }
+    return SGMV_OK;
+}
+
 int sgmv_set_fused_wait(double seconds) {
     if (!(seconds >= 0.0) || seconds > 10.0) return SGMV_ERR_BAD_SHAPE;
     unsigned long long b;

@@ -165,3 +165,17 @@ def test_lora_apply_multi_host_checks(lib):
     one = lib.lora_apply_workspace_bytes(64, 64, 4096, 4096, 16, 1)
     assert lib.lora_apply_multi_workspace_bytes(p, 2, 64, 64, 16, 1) >= one
     assert lib.lora_apply_multi_workspace_bytes(p, 0, 64, 64, 16, 1) == 0
+
+
+def test_load_adapter_host_checks(lib):
+    """Argument errors of sgmv_load_adapter come back before any copy."""
+    dummy = 0x1000  # never dereferenced: every call below fails a host check
+    L = lib.sgmv_load_adapter
+    assert L(dummy, dummy, 0, 1, 4, dummy, dummy, 64, 64, 8, 9, None) == 3
+    assert L(dummy, dummy, 4, 1, 4, dummy, dummy, 64, 64, 8, 1, None) == 2
+    assert L(dummy, dummy, 2, 3, 4, dummy, dummy, 64, 64, 8, 1, None) == 2
+    assert L(dummy, dummy, 0, 0, 4, dummy, dummy, 64, 64, 8, 1, None) == 2
+    assert L(dummy, dummy, -1, 1, 4, dummy, dummy, 64, 64, 8, 1, None) == 2
+    assert L(dummy, dummy, 0, 1, 4, dummy, dummy, 64, 64, 0, 1, None) == 2
+    assert L(None, dummy, 0, 1, 4, dummy, dummy, 64, 64, 8, 1, None) == 1
+    assert L(dummy, dummy, 0, 1, 4, dummy, None, 64, 64, 8, 1, None) == 1
