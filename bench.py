@@ -139,10 +139,11 @@ class BenchState:
         return g
 
 
-def run_gpu(w, steps: int, warmup: int, device="cuda:0", row_ids=None, projections=1):
+def run_gpu(w, steps: int, warmup: int, device="cuda:0", row_ids=None, projections=1,
+            warm=False):
     import torch
     per_set = (w.x.size + w.A.size + w.B.size + w.y0.size) * w.elem_bytes * projections
-    nsets = max(1, min(512, math.ceil(ROTATE_BYTES / max(per_set, 1))))
+    nsets = 1 if warm else max(1, min(512, math.ceil(ROTATE_BYTES / max(per_set, 1))))
     st = BenchState(w, nsets, device, row_ids, projections)
     for i in range(warmup):
         st.step(i)
@@ -310,6 +311,9 @@ def main(argv=None):
     ap.add_argument("--adapter-load", action="store_true",
                     help="instead: time on-demand loading of the workload's adapters from "
                          "pinned host memory into the device stacks (sgmv_load_adapter)")
+    ap.add_argument("--warm", action="store_true",
+                    help="no buffer rotation: the same inputs every step, resident in the "
+                         "256 MB Infinity Cache (a warm figure, not the HBM one)")
     ap.add_argument("--projections", type=int, default=1, choices=range(1, 9), metavar="P",
                     help="P add-ons of the workload's shape over the same batch in one "
                          "lora_apply_multi call (e.g. a layer's q/k/v/o projections)")
@@ -338,7 +342,7 @@ def main(argv=None):
         print(json.dumps(adapter_load(w)), flush=True)
         return 0
     P = args.projections
-    res = run_gpu(w, args.steps, args.warmup, row_ids=args.row_ids, projections=P)
+    res = run_gpu(w, args.steps, args.warmup, row_ids=args.row_ids, projections=P, warm=args.warm)
     step_s = res["gpu_ms"] / 1e3 / args.steps
     rows = int(w.seg_lengths.sum()) * P  # a row through one add-on is one SGMV row
     abytes = algorithmic_bytes(w) * P
@@ -362,6 +366,7 @@ def main(argv=None):
             "segments": w.num_segments, "adapters_in_stack": w.num_adapters, "scale": w.scale,
             "buffer_sets_rotated": res["nsets"], "launch": "hip graph of all timed steps",
             "projections": P,
+            "cache": "warm (inputs reused every step)" if args.warm else "cold (rotated buffers)",
             "segment_table": ("given" if args.row_ids is None
                               else f"built on the device from per-row ids ({args.row_ids})"),
         },
@@ -377,7 +382,8 @@ def main(argv=None):
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": measured_traffic(w.name) if args.row_ids is None and P == 1 else None,
+            "traffic": (measured_traffic(w.name)
+                        if args.row_ids is None and P == 1 and not args.warm else None),
             "algorithmic_bytes_per_launch": abytes,
             "tflops": flops / step_s / 1e12,
         },
