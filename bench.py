@@ -326,7 +326,7 @@ def main(argv=None):
         return 0
 
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
               "SGMV shards by segments with no exchange, so per-GPU throughput is the "
               "figure of interest.", file=sys.stderr)
         return 2
