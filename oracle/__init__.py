@@ -56,7 +56,10 @@ class Oracle:
                                            ctypes.c_double]
         lib.sgmv_oracle_lora_apply.argtypes = [dp, dp, fp, fp, fp, fp, ip, ip, _i32, _i32, _i32,
                                                _i32, _i32, _i32, ctypes.c_double]
-        for f in (lib.sgmv_oracle_shrink, lib.sgmv_oracle_expand, lib.sgmv_oracle_lora_apply):
+        lib.sgmv_oracle_lora_linear.argtypes = [dp, fp, fp, fp, fp, fp, ip, ip, _i32, _i32, _i32,
+                                                _i32, _i32, _i32, ctypes.c_double]
+        for f in (lib.sgmv_oracle_shrink, lib.sgmv_oracle_expand, lib.sgmv_oracle_lora_apply,
+                  lib.sgmv_oracle_lora_linear):
             f.restype = ctypes.c_int
         self.lib = lib
 
@@ -138,6 +141,33 @@ class Oracle:
             raise ValueError("oracle rejected the segment table or shapes")
         return y, v
 
+    def lora_linear(self, x, W, bias, A_stack, B_stack, seg_indptr, adapter_ids, scale):
+        """y = x @ W^T (+ bias) for every row, plus scale * (x A) B on the rows
+        of each segment.  W is [H2, H1]; bias is [H2] or None."""
+        x, W = self._f32(x), self._f32(W)
+        A, B = self._f32(A_stack), self._f32(B_stack)
+        seg, ids = self._segs(seg_indptr, adapter_ids)
+        R, H1 = x.shape
+        H2, H1w = W.shape
+        N, H1a, r = A.shape
+        if H1w != H1 or H1a != H1 or B.shape != (N, r, H2):
+            raise ValueError("shape mismatch between x, W and the stacks")
+        bp = None
+        if bias is not None:
+            bias = self._f32(bias)
+            if bias.shape != (H2,):
+                raise ValueError("bias must be [H2]")
+            bp = self._ptr(bias, ctypes.c_float)
+        y = np.empty((R, H2))
+        rc = self.lib.sgmv_oracle_lora_linear(
+            self._ptr(y, ctypes.c_double), self._ptr(x, ctypes.c_float),
+            self._ptr(W, ctypes.c_float), bp, self._ptr(A, ctypes.c_float),
+            self._ptr(B, ctypes.c_float), self._ptr(seg, _i32), self._ptr(ids, _i32),
+            ids.shape[0], R, N, H1, H2, r, float(scale))
+        if rc:
+            raise ValueError("oracle rejected the segment table or shapes")
+        return y
+
 
 _default: Oracle | None = None
 
@@ -162,3 +192,7 @@ def expand(*args, **kwargs):
 
 def lora_apply(*args, **kwargs):
     return get().lora_apply(*args, **kwargs)
+
+
+def lora_linear(*args, **kwargs):
+    return get().lora_linear(*args, **kwargs)

@@ -12,8 +12,9 @@
  *   LoRA forward: the output of an adapted linear layer is the base product
  *   plus a low-rank correction, y = xW + xAB, with A of shape [H1, r] and B of
  *   shape [r, H2]  (Punica walkthrough, omica.com.cn/news/959180, section 2.1).
- *   Only the correction xAB is computed here; the base xW belongs to the
- *   caller and is already inside y on entry.
+ *   The shrink, expand and lora_apply functions compute only the correction
+ *   xAB: the base xW belongs to the caller and is already inside y on entry.
+ *   sgmv_oracle_lora_linear computes the whole layer, base product included.
  *
  *   Many requests, each with its own adapter, are served in one batch: the
  *   correction for request i is x_i A_i B_i, evaluated in two steps, first the
@@ -47,6 +48,7 @@
  */
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 static int check_segments(const int32_t* seg_indptr, const int32_t* adapter_ids,
                           int32_t num_segments, int32_t num_rows, int32_t num_adapters)
@@ -128,4 +130,42 @@ int sgmv_oracle_lora_apply(double* y, double* v, const float* y0, const float* x
                            num_rows, num_adapters, H1, r)) return -1;
     return sgmv_oracle_expand(y, v, B_stack, seg_indptr, adapter_ids, num_segments,
                               num_rows, num_adapters, r, H2, scale);
+}
+
+/* An adapted linear layer for one batch, base product included: for every
+ * row i and column j
+ *     y[i][j] = sum over h of x[i][h] * W[j][h]  (+ bias[j])
+ * and then, for the rows of each segment, the add-on scale * (x_i A_a) B_a,
+ * i.e. y = xW + xAB of Punica walkthrough (omica.com.cn/news/959180, section
+ * 2.1) with the base layer folded in, as the fused kernel of aivaro.ru answer
+ * 959 (section 3.2) does.  W is stored [H2][H1] (output feature major, each
+ * row the weights of one output), so the page's W is its transpose; bias may
+ * be NULL.  Rows outside every segment receive the base product only.      */
+int sgmv_oracle_lora_linear(double* y, const float* x, const float* W, const float* bias,
+                            const float* A_stack, const float* B_stack,
+                            const int32_t* seg_indptr, const int32_t* adapter_ids,
+                            int32_t num_segments, int32_t num_rows, int32_t num_adapters,
+                            int32_t H1, int32_t H2, int32_t r, double scale)
+{
+    if (H1 < 0 || H2 < 0 || r < 0) return -1;
+    if (check_segments(seg_indptr, adapter_ids, num_segments, num_rows, num_adapters)) return -1;
+    for (int64_t i = 0; i < num_rows; ++i) {
+        const float* xr = x + i * (int64_t)H1;
+        for (int64_t j = 0; j < H2; ++j) {
+            const float* wr = W + j * (int64_t)H1;
+            double acc = 0.0;
+            for (int64_t h = 0; h < H1; ++h)
+                acc += (double)xr[h] * (double)wr[h];
+            y[i * H2 + j] = bias ? acc + (double)bias[j] : acc;
+        }
+    }
+    double* v = (double*)calloc((size_t)num_rows * (size_t)(r > 0 ? r : 1), sizeof(double));
+    if (!v) return -1;
+    int rc = sgmv_oracle_shrink(v, x, A_stack, seg_indptr, adapter_ids, num_segments,
+                                num_rows, num_adapters, H1, r);
+    if (!rc)
+        rc = sgmv_oracle_expand(y, v, B_stack, seg_indptr, adapter_ids, num_segments,
+                                num_rows, num_adapters, r, H2, scale);
+    free(v);
+    return rc;
 }

@@ -247,6 +247,59 @@ def pin_rejects_malformed_tables(orc):
         raise AssertionError(f"malformed table accepted: {seg} {ids}")
 
 
+# -- the adapted linear layer (base product folded in) --------------------------
+
+def _linear_case(seed, H1=24, H2=20, r=4, N=5, R=11, S=4, bias=True):
+    w = _small(seed=seed, H1=H1, H2=H2, r=r, N=N, R=R, S=S)
+    W, b = wl.base_layer(seed, "f32", H1, H2, bias=bias)
+    return w, W, b
+
+
+def pin_linear_single_segment_is_matmul(orc):
+    """One segment over every row: y = x W^T + b + s (x A_a) B_a, numpy fp64."""
+    w, W, b = _linear_case(21, H1=40, H2=28, r=6, R=9)
+    seg, ids = np.array([0, 9], np.int32), np.array([3], np.int32)
+    y = orc.lora_linear(w.x, W, b, w.A, w.B, seg, ids, w.scale)
+    x = w.x.astype(np.float64)
+    ref = (x @ W.T.astype(np.float64) + b.astype(np.float64)
+           + w.scale * ((x @ w.A[3].astype(np.float64)) @ w.B[3].astype(np.float64)))
+    _rel_close(y, ref, 1e-12)
+
+
+def pin_linear_integer_exact(orc):
+    """{-1,0,1} x, W, A, B and integer bias over several segments (one empty,
+    one adapter named twice, uncovered rows at both ends): int64 arithmetic
+    gives the exact answer, bit for bit."""
+    w = wl.integer_exact(6, "f32", 72, 40, 8, 6, 26, 3, density=0.3, scale=2.0)
+    W, b = wl.base_layer(6, "f32", 72, 40, integer=True, density=0.3)
+    seg = np.array([2, 9, 9, 15, 23], np.int32)
+    ids = np.array([4, 1, 4, 0], np.int32)
+    y = orc.lora_linear(w.x, W, b, w.A, w.B, seg, ids, 2.0)
+    xi = w.x.astype(np.int64)
+    ref = xi @ W.astype(np.int64).T + b.astype(np.int64)
+    for s in range(4):
+        lo, hi, a = int(seg[s]), int(seg[s + 1]), int(ids[s])
+        ref[lo:hi] += 2 * ((xi[lo:hi] @ w.A[a].astype(np.int64)) @ w.B[a].astype(np.int64))
+    assert np.array_equal(y, ref.astype(np.float64))
+
+
+def pin_linear_bias_and_uncovered_rows(orc):
+    """No bias equals a zero bias; rows outside every segment get exactly the
+    base product (numpy fp64), and the bias shifts every row by b."""
+    w, W, b = _linear_case(22, R=13, S=3)
+    seg = np.array([3, 5, 8, 10], np.int32)
+    ids = np.array([1, 4, 2], np.int32)
+    y_nb = orc.lora_linear(w.x, W, None, w.A, w.B, seg, ids, w.scale)
+    y_zb = orc.lora_linear(w.x, W, np.zeros_like(b), w.A, w.B, seg, ids, w.scale)
+    assert np.array_equal(y_nb, y_zb)
+    y_b = orc.lora_linear(w.x, W, b, w.A, w.B, seg, ids, w.scale)
+    _rel_close(y_b - y_nb, np.broadcast_to(b.astype(np.float64), y_b.shape), 1e-12)
+    base = w.x.astype(np.float64) @ W.T.astype(np.float64)
+    out = [0, 1, 2, 10, 11, 12]
+    _rel_close(y_nb[out], base[out], 1e-12)
+    assert not np.allclose(y_nb[3:10], base[3:10])
+
+
 ALL_PINS = [
     pin_hand_worked_example,
     pin_single_segment_is_matmul,
@@ -261,4 +314,7 @@ ALL_PINS = [
     pin_split_merge_same_adapter,
     pin_shrink_expand_compose,
     pin_rejects_malformed_tables,
+    pin_linear_single_segment_is_matmul,
+    pin_linear_integer_exact,
+    pin_linear_bias_and_uncovered_rows,
 ]

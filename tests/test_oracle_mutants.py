@@ -31,6 +31,13 @@ MUTANTS = [
     ("adapter_stride_wrong", "a * (int64_t)H1 * r", "a * (int64_t)H1", None),
     ("y_not_initialised", "y[e] = (double)y0[e];", "y[e] = 0.0;", None),
     ("v_row_stride_wrong", "v[i * r + k] = acc;", "v[i + k] = acc;", None),
+    ("W_transposed", "(double)wr[h]", "(double)W[h * H2 + j]", None),
+    ("W_row_of_input", "W + j * (int64_t)H1", "W + i * (int64_t)H1", None),
+    ("linear_bias_dropped", "acc + (double)bias[j]", "acc", None),
+    ("linear_bias_wrong_index", "(double)bias[j]", "(double)bias[0]", None),
+    ("linear_x_row_zero", "x + i * (int64_t)H1", "x", None),
+    ("linear_addon_skipped", "if (!rc)\n        rc = sgmv_oracle_expand", "if (0)\n        rc = sgmv_oracle_expand", None),
+    ("linear_base_sign_flipped", "y[i * H2 + j] = bias ? acc", "y[i * H2 + j] = bias ? -acc", None),
 ]
 
 

@@ -250,3 +250,28 @@ def integer_exact(seed, dtype, H1, H2, r, num_adapters, num_rows, num_segments,
     y0 = rng.integers(-8, 9, size=(num_rows, H2)).astype(np.float32)
     return Workload(f"intexact_{dtype}_{H1}x{H2}_r{r}", dtype, H1, H2, r, num_adapters,
                     seg, ids, float(scale), x, A, B, y0)
+
+
+# -- base layer of an adapted linear layer --------------------------------------
+
+def base_layer(seed, dtype, H1, H2, bias=True, integer=False, density=0.05):
+    """Weight W [H2, H1] (one row per output feature) and bias [H2] or None.
+
+    From their own generator, numpy.random.default_rng(seed + 1000003), so
+    that adding a base layer changes none of a workload's other draws.
+    Floating: W and bias ~ U(-1/sqrt(H1), 1/sqrt(H1)), the usual initial
+    range of a linear layer, rounded to the dtype.  integer=True: W sparse
+    {-1, 0, 1} with the given density and bias small integers, so that with
+    the integer_exact add-on every partial sum is a small integer.
+    """
+    rng = np.random.default_rng(seed + 1000003)
+    if integer:
+        mag = rng.random((H2, H1)) < density
+        sign = np.where(rng.random((H2, H1)) < 0.5, -1.0, 1.0)
+        W = (mag * sign).astype(np.float32)
+        b = rng.integers(-8, 9, size=H2).astype(np.float32) if bias else None
+        return W, b
+    bound = np.float32(1.0 / np.sqrt(H1))
+    W = rng.random((H2, H1), dtype=np.float32) * (2 * bound) - bound
+    b = (rng.random(H2, dtype=np.float32) * (2 * bound) - bound) if bias else None
+    return round_to_dtype(W, dtype), (None if b is None else round_to_dtype(b, dtype))
