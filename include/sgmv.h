@@ -200,12 +200,51 @@ int lora_apply_multi(const sgmv_lora_problem* problems, int32_t num_problems,
                      void* stream);
 
 /*
+ * Adapted linear layer with the base product fused in:
+ *   y[i, :] = round(x[i, :] @ W^T + bias + scale * (x[i, :] @ A_a) @ B_a)
+ * for every row i, a = adapter_ids of row i's segment; rows outside every
+ * segment (or in a segment whose adapter id is outside [0, num_adapters))
+ * get round(x[i, :] @ W^T + bias).  This is the layer y = xW + xAB of Punica
+ * walkthrough (omica.com.cn/news/959180, section 2.1) computed as one fused
+ * kernel over the output, the correction added to each base tile before it
+ * is stored (aivaro.ru answer 959, section 3.2: fusing the LoRA transform
+ * into the base linear layer saves memory traffic), so y is written once
+ * and never read.
+ *
+ * y: [num_rows, H2], overwritten.  x: [num_rows, H1].  W: [H2, H1], the row
+ * of weights of each output feature (the usual layout of a linear layer's
+ * weight; the page's W is its transpose).  bias: [H2] or NULL.  The stacks
+ * and the segment table are those of lora_apply; with num_segments == 0
+ * they may be NULL and the call computes the base layer alone.  All sums
+ * are taken in float32 and y is rounded once.
+ *
+ * fp16/bf16 with H1 and H2 multiples of 8 and 16-byte aligned x, W, y,
+ * bias and B_stack run on the matrix cores; any other call (float32
+ * included) takes a slow element-wise kernel with the same definition.
+ * The call enqueues two launches: the shrink of the add-on (skipped when
+ * num_segments == 0), then the fused layer.
+ *
+ * workspace: at least lora_linear_workspace_bytes(...) bytes, with the
+ * conventions of "Workspace" above.  Returns as lora_apply; num_rows == 0
+ * is a no-op.
+ */
+size_t lora_linear_workspace_bytes(int32_t num_rows, int32_t num_segments, int32_t H1,
+                                   int32_t H2, int32_t r, int32_t dtype);
+int lora_linear(void* y, const void* x, const void* W, const void* bias,
+                const void* A_stack, const void* B_stack,
+                const int32_t* seg_indptr, const int32_t* adapter_ids,
+                int32_t num_segments, int32_t num_rows, int32_t num_adapters,
+                int32_t H1, int32_t H2, int32_t r, float scale, int32_t dtype,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * On-demand adapter loading: copies `count` adapters from HOST memory into
  * slots [slot, slot + count) of the device stacks -- h_A [count, H1, r]
  * into A_stack[slot ..] and h_B [count, r, H2] into B_stack[slot ..], all
  * row-major in the stacks' dtype -- with two asynchronous copies on
- * `stream`, so that the next lora_apply on that stream sees them.  Adapters not yet resident are brought in this way when a
- * request needs them (Punica review, nubint.ai, "Proposed method": the
+ * `stream`, so that the next lora_apply on that stream sees them.  Adapters
+ * not yet resident are brought in this way when a request needs them
+ * (Punica review, nubint.ai, "Proposed method": the
  * system loads LoRA models on demand and keeps only the base model
  * resident).  For the copy to overlap other work the host buffers must be
  * pinned (hipHostMalloc); pageable buffers are staged by the runtime.  The

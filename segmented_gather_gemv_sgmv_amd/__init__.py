@@ -67,6 +67,9 @@ ABI = [
     ("lora_apply_multi_workspace_bytes", _sz, [_vp, _i32, _i32, _i32, _i32, _i32]),
     ("lora_apply_multi", ctypes.c_int, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp,
                                         _sz, _vp]),
+    ("lora_linear_workspace_bytes", _sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    ("lora_linear", ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                   _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
 ]
 
 
@@ -261,6 +264,55 @@ def lora_apply(y, x, A_stack, B_stack, seg_indptr, adapter_ids, scale=1.0, works
     return y
 
 
+def lora_linear_workspace_bytes(num_rows, num_segments, H1, H2, r, dtype) -> int:
+    return int(lib().lora_linear_workspace_bytes(num_rows, num_segments, H1, H2, r,
+                                                 dtype_code(dtype)))
+
+
+def lora_linear(x, W, A_stack, B_stack, seg_indptr, adapter_ids, scale=1.0, bias=None,
+                out=None, workspace=None):
+    """Adapted linear layer, base product fused in: returns
+    y = x @ W.T (+ bias) + scale * (x @ A_stack[a]) @ B_stack[a] per row of
+    each segment (base product only on other rows), float32 sums, rounded
+    once.  W is [H2, H1] (torch's linear weight layout), bias [H2] or None.
+    ``out`` (optional) receives y; ``workspace`` as for lora_apply."""
+    torch = _torch()
+    dev = x.device
+    _need(x, "x", dev, None, 2)
+    _need(W, "W", dev, x.dtype, 2)
+    _need(A_stack, "A_stack", dev, x.dtype, 3)
+    _need(B_stack, "B_stack", dev, x.dtype, 3)
+    S = _segments(seg_indptr, adapter_ids, dev)
+    R, H1 = x.shape
+    H2, H1w = W.shape
+    N, H1a, r = A_stack.shape
+    if H1w != H1 or H1a != H1 or tuple(B_stack.shape) != (N, r, H2):
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)}, W {tuple(W.shape)}, "
+                         f"A_stack {tuple(A_stack.shape)}, B_stack {tuple(B_stack.shape)}")
+    if bias is not None:
+        _need(bias, "bias", dev, x.dtype, 1)
+        if bias.shape[0] != H2:
+            raise ValueError(f"bias must be [{H2}], got {tuple(bias.shape)}")
+    if out is None:
+        out = torch.empty((R, H2), dtype=x.dtype, device=dev)
+    else:
+        _need(out, "out", dev, x.dtype, 2)
+        if tuple(out.shape) != (R, H2):
+            raise ValueError(f"out must be {(R, H2)}, got {tuple(out.shape)}")
+    dt = dtype_code(x.dtype)
+    stream = _stream_ptr(dev)
+    need = lora_linear_workspace_bytes(R, S, H1, H2, r, x.dtype)
+    if workspace is None:
+        workspace = _workspaces.get(dev, stream, need)
+    _check(lib().lora_linear(out.data_ptr(), x.data_ptr(), W.data_ptr(),
+                             None if bias is None else bias.data_ptr(), A_stack.data_ptr(),
+                             B_stack.data_ptr(), seg_indptr.data_ptr(), adapter_ids.data_ptr(),
+                             S, R, N, H1, H2, r, float(scale), dt, workspace.data_ptr(),
+                             workspace.numel() * workspace.element_size(), stream),
+           "lora_linear")
+    return out
+
+
 def lora_apply_multi_workspace_bytes(shapes, num_rows, num_segments, r, dtype) -> int:
     """Workspace bytes of a lora_apply_multi call whose problems have the
     given (H1, H2) shapes."""
@@ -412,6 +464,7 @@ def group_rows(row_ids, num_adapters: int, out=None):
 
 
 __all__ = [
+    "lora_linear", "lora_linear_workspace_bytes",
     "build_segments", "group_rows", "lora_apply_multi", "lora_apply_multi_workspace_bytes",
     "load_adapter",
     "LoraProblem",

@@ -21,6 +21,7 @@
 #include "sgmv_fused.hpp"
 #include "sgmv_mfma.hpp"
 #include "sgmv_segments.hpp"
+#include "sgmv_linear.hpp"
 
 namespace {
 
@@ -438,6 +439,71 @@ bool grid_fits(const Plan& p, int H2) {
            slots * csplit_vec <= kMaxGrid;
 }
 
+// -- adapted linear layer ------------------------------------------------------
+// Skinny tiles for decode-sized batches (64 rows: the whole batch, x shared
+// by the four waves through LDS, four chunks of loads in flight to stream
+// W), square tiles for many rows (each operand read once per 128 rows or
+// columns of output).
+using LinSkinny = LinearShape<1, 4, 4, 1, 4>;
+using LinSquare = LinearShape<2, 2, 4, 4, 2>;
+constexpr int kLinTargetWorkgroups = 512;  // split K until the grid has this many
+
+struct LinearPlan {
+    int cfg;  // 0 skinny tiles, 1 square tiles, -1 the element-wise kernel
+    int BM, BN;
+    long long tiles_m, tiles_n, tiles;
+    int ksplit, cps;  // K ranges per tile and chunks of 64 per range
+    Plan shrink;      // the preceding shrink launch (its ksplit = v's partials)
+};
+
+// Pure function of the shapes, so that the workspace size can be queried.
+LinearPlan make_linear_plan(int M, int S, int H1, int H2, int r, int dtype) {
+    LinearPlan lp{};
+    lp.shrink = make_plan(M, S, H1, r, dtype);
+    lp.cfg = -1;
+    lp.ksplit = 1;
+    if (dtype == SGMV_F32 || H1 % 8 != 0 || H2 % 8 != 0) return lp;
+    lp.cfg = M <= LinSkinny::kBM ? 0 : 1;
+    lp.BM = lp.cfg == 0 ? LinSkinny::kBM : LinSquare::kBM;
+    lp.BN = lp.cfg == 0 ? LinSkinny::kBN : LinSquare::kBN;
+    lp.tiles_m = (M + lp.BM - 1) / lp.BM;
+    lp.tiles_n = (H2 + lp.BN - 1) / lp.BN;
+    lp.tiles = lp.tiles_m * lp.tiles_n;
+    const int nk = (H1 + kLinBK - 1) / kLinBK;
+    long long k = 1;
+    if (lp.tiles < kLinTargetWorkgroups && lp.tiles <= kCounterSlots) {
+        k = (kLinTargetWorkgroups + lp.tiles - 1) / lp.tiles;
+        const long long kmax = nk / 2 > 1 ? nk / 2 : 1;  // at least two chunks per range
+        if (k > kmax) k = kmax;
+    }
+    lp.cps = (int)((nk + k - 1) / k);
+    lp.ksplit = (nk + lp.cps - 1) / lp.cps;
+    return lp;
+}
+
+size_t linear_v_bytes(const LinearPlan& lp, int M, int r) {
+    return round256((size_t)lp.shrink.ksplit * (size_t)M * (size_t)r * sizeof(float));
+}
+
+size_t linear_part_bytes(const LinearPlan& lp) {
+    if (lp.cfg < 0 || lp.ksplit <= 1) return 0;
+    return (size_t)lp.tiles * (size_t)lp.ksplit * (size_t)lp.BM * (size_t)lp.BN * sizeof(float);
+}
+
+template <typename DT, typename SH>
+void launch_linear_tiled(void* y, const void* x, const void* W, const void* bias, const void* B,
+                         const float* vpart, long long vstride, int vsplit, const int32_t* seg,
+                         const int32_t* ids, int S, int M, int nad, int H1, int H2, int r,
+                         float scale, float* part, int* counters, const LinearPlan& lp,
+                         hipStream_t st) {
+    using T = typename DT::storage;
+    const unsigned grid = (unsigned)(lp.tiles * lp.ksplit);
+    launch(&linear_lora_kernel<DT, SH>, dim3(grid), dim3(kLinThreads), st, (T*)y, (const T*)x,
+           (const T*)W, (const T*)bias, (const T*)B, vpart, vstride, vsplit, seg, ids, S, M, nad,
+           H1, H2, r, scale, part, counters, kCounterStride, lp.ksplit, lp.cps, (int)lp.tiles_n,
+           (int)lp.tiles);
+}
+
 }  // namespace
 
 extern "C" {
@@ -831,6 +897,75 @@ int sgmv_load_adapter(void* A_stack, void* B_stack, int32_t slot, int32_t count,
         return SGMV_ERR_HIP;
     }
     return SGMV_OK;
+}
+
+size_t lora_linear_workspace_bytes(int32_t num_rows, int32_t num_segments, int32_t H1, int32_t H2,
+                                   int32_t r, int32_t dtype) {
+    if (check_common(num_segments, num_rows, 0, r, dtype) != SGMV_OK || H1 < 1 || H2 < 1) return 0;
+    const LinearPlan lp = make_linear_plan(num_rows, num_segments, H1, H2, r, dtype);
+    return kCounterBytes + linear_v_bytes(lp, num_rows, r) + linear_part_bytes(lp);
+}
+
+int lora_linear(void* y, const void* x, const void* W, const void* bias, const void* A_stack,
+                const void* B_stack, const int32_t* seg_indptr, const int32_t* adapter_ids,
+                int32_t num_segments, int32_t num_rows, int32_t num_adapters, int32_t H1,
+                int32_t H2, int32_t r, float scale, int32_t dtype, void* workspace,
+                size_t workspace_bytes, void* stream) {
+    int rc = check_common(num_segments, num_rows, num_adapters, r, dtype);
+    if (rc != SGMV_OK) return rc;
+    if (H1 < 1 || H2 < 1) return SGMV_ERR_BAD_SHAPE;
+    if (num_rows == 0) return SGMV_OK;
+    if (!y || !x || !W) return SGMV_ERR_NULL_PTR;
+    if (num_segments > 0 && (!A_stack || !B_stack || !seg_indptr || !adapter_ids))
+        return SGMV_ERR_NULL_PTR;
+    const LinearPlan lp = make_linear_plan(num_rows, num_segments, H1, H2, r, dtype);
+    if (num_segments > 0 && !grid_fits(lp.shrink, 1)) return SGMV_ERR_UNSUPPORTED;
+    if (lp.cfg >= 0 ? lp.tiles * lp.ksplit > kMaxGrid
+                    : ((long long)num_rows * H2 + 255) / 256 > kMaxGrid)
+        return SGMV_ERR_UNSUPPORTED;
+    const size_t need = lora_linear_workspace_bytes(num_rows, num_segments, H1, H2, r, dtype);
+    if (!workspace || workspace_bytes < need) return SGMV_ERR_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    int* counters = (int*)workspace;
+    float* vpart = (float*)((char*)workspace + kCounterBytes);
+    float* part = (float*)((char*)vpart + linear_v_bytes(lp, num_rows, r));
+    const long long vstride = (long long)num_rows * r;
+    const int vsplit = lp.shrink.ksplit;
+    if (num_segments > 0) {
+        with_dtype(dtype, [&](auto dt) {
+            using DT = decltype(dt);
+            dispatch_shrink<DT>(vpart, vstride, x, A_stack, seg_indptr, adapter_ids, num_segments,
+                                num_rows, num_adapters, H1, r, lp.shrink, st);
+        });
+        if ((rc = launch_status()) != SGMV_OK) return rc;
+    }
+    const bool tiled = lp.cfg >= 0 && aligned16(x) && aligned16(W) && aligned16(y) &&
+                       aligned16(B_stack) && aligned16(bias);
+    with_dtype(dtype, [&](auto dt) {
+        using DT = decltype(dt);
+        using T = typename DT::storage;
+        if constexpr (!std::is_same<DT, F32>::value) {
+            if (tiled) {
+                if (lp.cfg == 0)
+                    launch_linear_tiled<DT, LinSkinny>(y, x, W, bias, B_stack, vpart, vstride,
+                                                       vsplit, seg_indptr, adapter_ids,
+                                                       num_segments, num_rows, num_adapters, H1,
+                                                       H2, r, scale, part, counters, lp, st);
+                else
+                    launch_linear_tiled<DT, LinSquare>(y, x, W, bias, B_stack, vpart, vstride,
+                                                       vsplit, seg_indptr, adapter_ids,
+                                                       num_segments, num_rows, num_adapters, H1,
+                                                       H2, r, scale, part, counters, lp, st);
+                return;
+            }
+        }
+        const unsigned grid = (unsigned)(((long long)num_rows * H2 + 255) / 256);
+        launch(&linear_lora_generic_kernel<DT>, dim3(grid), dim3(256), st, (T*)y, (const T*)x,
+               (const T*)W, (const T*)bias, (const T*)B_stack, (const float*)vpart, vstride,
+               vsplit, seg_indptr, adapter_ids, num_segments, num_rows, num_adapters, H1, H2, r,
+               scale);
+    });
+    return launch_status();
 }
 
 int sgmv_set_fused_wait(double seconds) {

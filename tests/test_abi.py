@@ -179,3 +179,46 @@ def test_load_adapter_host_checks(lib):
     assert L(dummy, dummy, 0, 1, 4, dummy, dummy, 64, 64, 0, 1, None) == 2
     assert L(None, dummy, 0, 1, 4, dummy, dummy, 64, 64, 8, 1, None) == 1
     assert L(dummy, dummy, 0, 1, 4, dummy, None, 64, 64, 8, 1, None) == 1
+
+
+def _linear(lib, **kw):
+    a = dict(y=FAKE, x=FAKE, W=FAKE, bias=None, A=FAKE, B=FAKE, seg=FAKE, ids=FAKE, S=4, R=16,
+             N=4, H1=256, H2=256, r=8, scale=1.0, dtype=1, ws=FAKE, ws_bytes=1 << 30,
+             stream=None)
+    a.update(kw)
+    return lib.lora_linear(a["y"], a["x"], a["W"], a["bias"], a["A"], a["B"], a["seg"], a["ids"],
+                           a["S"], a["R"], a["N"], a["H1"], a["H2"], a["r"], a["scale"],
+                           a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_lora_linear_host_checks(lib):
+    assert _linear(lib, dtype=9) == 3
+    assert _linear(lib, r=0) == 2
+    assert _linear(lib, H1=0) == 2
+    assert _linear(lib, H2=0) == 2
+    assert _linear(lib, R=-1) == 2
+    for p in ("y", "x", "W", "A", "B", "seg", "ids"):
+        assert _linear(lib, **{p: None}) == 1, p
+    # without segments the stacks and the table are not needed ...
+    need0 = lib.lora_linear_workspace_bytes(16, 0, 256, 256, 8, 1)
+    assert _linear(lib, S=0, A=None, B=None, seg=None, ids=None, ws=None, ws_bytes=need0) == 5
+    # ... and an empty batch enqueues nothing at all
+    assert _linear(lib, R=0, y=None, x=None, W=None, ws=None, ws_bytes=0) == 0
+    need = lib.lora_linear_workspace_bytes(16, 4, 256, 256, 8, 1)
+    assert need > 256 * 1024
+    assert _linear(lib, ws=None, ws_bytes=need) == 5
+    assert _linear(lib, ws_bytes=need - 1) == 5
+
+
+def test_lora_linear_workspace_sizes(lib):
+    counters = 256 * 1024
+    for R, S, H1, H2, r, dt in [(64, 64, 4096, 4096, 16, 1), (4096, 16, 4096, 4096, 16, 1),
+                                (256, 110, 5120, 13824, 64, 2), (16, 4, 256, 256, 8, 0),
+                                (7, 3, 100, 90, 5, 1), (5, 0, 64, 64, 4, 2)]:
+        n = lib.lora_linear_workspace_bytes(R, S, H1, H2, r, dt)
+        assert n >= counters + R * r * 4
+        assert n == lib.lora_linear_workspace_bytes(R, S, H1, H2, r, dt)
+    # decode shapes split K over workgroups and keep float32 partial tiles
+    assert (lib.lora_linear_workspace_bytes(64, 64, 4096, 4096, 16, 1)
+            > lib.lora_apply_workspace_bytes(64, 64, 4096, 4096, 16, 1))
+    assert lib.lora_linear_workspace_bytes(16, 4, 256, 256, 0, 1) == 0
