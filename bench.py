@@ -194,6 +194,76 @@ def measured_traffic(workload_name: str):
     return t.get("traffic_bytes_per_launch")
 
 
+def run_linear(w, mode: str, steps: int, warmup: int, device="cuda:0"):
+    """Times the adapted linear layer y = x W^T + bias + s (x A_a) B_a over the
+    workload's batch: ``fused`` is one lora_linear call, ``unfused`` is
+    torch's addmm for the base product followed by lora_apply.  W [H2, H1]
+    and bias are seeded N(0, 1/H1) and N(0, 1) draws in the workload's dtype;
+    buffers rotate over >= 1 GiB as in run_gpu and the timed steps run as one
+    HIP graph."""
+    import torch
+    import segmented_gather_gemv_sgmv_amd as sg
+    dt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[w.dtype]
+    dev = torch.device(device)
+    rng = np.random.default_rng(1)
+    W0 = torch.from_numpy(rng.standard_normal((w.H2, w.H1), dtype=np.float32)
+                          / np.float32(math.sqrt(w.H1))).to(dev).to(dt)
+    b0 = torch.from_numpy(rng.standard_normal(w.H2, dtype=np.float32)).to(dev).to(dt)
+    to = lambda a: torch.from_numpy(a).to(dev).to(dt)
+    x0, A0, B0 = to(w.x), to(w.A), to(w.B)
+    seg = torch.from_numpy(w.seg_indptr).to(dev)
+    ids = torch.from_numpy(w.adapter_ids).to(dev)
+    e = w.elem_bytes
+    per_set = (W0.numel() + x0.numel() + A0.numel() + B0.numel() + w.num_rows * w.H2) * e
+    nsets = max(1, min(256, math.ceil(ROTATE_BYTES / per_set)))
+    sets = [dict(W=W0 if i == 0 else W0.clone(), b=b0 if i == 0 else b0.clone(),
+                 x=x0 if i == 0 else x0.clone(), A=A0 if i == 0 else A0.clone(),
+                 B=B0 if i == 0 else B0.clone(),
+                 y=torch.empty((w.num_rows, w.H2), dtype=dt, device=dev)) for i in range(nsets)]
+    nbytes = max(sg.lora_linear_workspace_bytes(w.num_rows, w.num_segments, w.H1, w.H2, w.r, dt),
+                 sg.lora_apply_workspace_bytes(w.num_rows, w.num_segments, w.H1, w.H2, w.r, dt))
+    ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        s = sets[i % nsets]
+        if mode == "fused":
+            sg.lora_linear(s["x"], s["W"], s["A"], s["B"], seg, ids, w.scale, bias=s["b"],
+                           out=s["y"], workspace=ws)
+        else:
+            torch.addmm(s["b"], s["x"], s["W"].t(), out=s["y"])
+            sg.lora_apply(s["y"], s["x"], s["A"], s["B"], seg, ids, w.scale, workspace=ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize(dev)
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        step(warmup)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize(dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for k in range(steps):
+            step(warmup + k)
+    torch.cuda.synchronize(dev)
+    stream = torch.cuda.current_stream(dev)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    g.replay()
+    end.record(stream)
+    torch.cuda.synchronize(dev)
+    us = start.elapsed_time(end) * 1e3 / steps
+    # What the fused layer must move: W, bias, x, y written once, each
+    # segment's adapter.
+    segs = int((w.seg_lengths > 0).sum())
+    abytes = (w.H1 * w.H2 + w.H2 + w.num_rows * (w.H1 + w.H2) + segs * w.r * (w.H1 + w.H2)) * e
+    return {"mode": mode, "workload": w.name, "us_per_call": us, "buffer_sets_rotated": nsets,
+            "algorithmic_bytes": abytes, "achieved_hbm_GBps": abytes / us / 1e3,
+            "hbm_peak_frac": abytes / us / 1e3 / HBM_PEAK_GBPS,
+            "base_flops_TFLOPs": 2.0 * w.num_rows * w.H1 * w.H2 / us / 1e6}
+
+
 def copy_calibration(nbytes: int, reps: int = 20):
     """A plain device-to-device copy of known size, for scaling the
     FETCH_SIZE / WRITE_SIZE counters (run it under rocprofv3 --pmc)."""
@@ -317,6 +387,9 @@ def main(argv=None):
     ap.add_argument("--projections", type=int, default=1, choices=range(1, 9), metavar="P",
                     help="P add-ons of the workload's shape over the same batch in one "
                          "lora_apply_multi call (e.g. a layer's q/k/v/o projections)")
+    ap.add_argument("--linear", choices=("fused", "unfused"), default=None,
+                    help="instead: time the adapted linear layer over the workload's batch, "
+                         "base product fused in (lora_linear) or not (addmm + lora_apply)")
     ap.add_argument("--workload", default="llama7b_decode", choices=sorted(WORKLOADS),
                     help="workload to time (default: the Llama-2-7B decode projection); the "
                          "others are the remaining seeded configurations")
@@ -340,6 +413,9 @@ def main(argv=None):
     w = WORKLOADS[args.workload](wl)
     if args.adapter_load:
         print(json.dumps(adapter_load(w)), flush=True)
+        return 0
+    if args.linear:
+        print(json.dumps(run_linear(w, args.linear, args.steps, args.warmup)), flush=True)
         return 0
     P = args.projections
     res = run_gpu(w, args.steps, args.warmup, row_ids=args.row_ids, projections=P, warm=args.warm)
