@@ -100,6 +100,158 @@ __device__ __forceinline__ int row_adapter(P seg_indptr, P adapter_ids, int S, i
     return (a >= 0 && a < num_adapters) ? a : -1;
 }
 
+// The part of an adapted-linear tile that follows the base product, shared
+// by the tile kernels.  On entry s_t holds the tile's float32 base product
+// for this workgroup's K range ([BM][TP], written by the caller; the barrier
+// here makes it visible).  Finds each row's adapter, adds this workgroup's
+// share of the ranks of scale * v B_a, combines the K ranges (the last
+// workgroup of a tile to arrive sums them in a fixed order), adds the bias,
+// rounds once and stores y.
+template <typename DT, int BM, int BN, int TP>
+__device__ __forceinline__ void linear_finish(
+    const float* s_t, int* s_aid, float* s_v, const int* s_seg, const int* s_ids, int* s_last,
+    bool seg_lds, typename DT::storage* __restrict__ y,
+    const typename DT::storage* __restrict__ bias,
+    const typename DT::storage* __restrict__ B_stack, const float* __restrict__ vpart,
+    long long vstride, int vsplit, const int* __restrict__ seg_indptr,
+    const int* __restrict__ adapter_ids, int S, int M, int num_adapters, int H2, int r,
+    float scale, float* __restrict__ part, int* __restrict__ counters, int counter_stride,
+    int ksplit, int q, int t, int m0, int n0) {
+    constexpr int kPieces = BM * BN / 8 / kLinThreads;
+    static_assert(BM * BN % (8 * kLinThreads) == 0, "uneven epilogue");
+    const int tid = threadIdx.x;
+    // Adapter of each tile row.
+    for (int i = tid; i < BM; i += kLinThreads) {
+        int a = -1;
+        if (m0 + i < M)
+            a = seg_lds ? row_adapter((const int*)s_seg, (const int*)s_ids, S, m0 + i, num_adapters)
+                        : row_adapter(seg_indptr, adapter_ids, S, m0 + i, num_adapters);
+        s_aid[i] = a;
+    }
+
+    __syncthreads();  // s_aid, and the caller's s_t
+
+    // ---- epilogue: row-contiguous pieces of 8 columns --------------------
+    float val[kPieces][8];
+#pragma unroll
+    for (int u = 0; u < kPieces; ++u) {
+        const int pid = tid + u * kLinThreads;
+        const int il = pid / (BN / 8), c8 = pid % (BN / 8);
+        const float4 lo = *reinterpret_cast<const float4*>(s_t + il * TP + c8 * 8);
+        const float4 hi = *reinterpret_cast<const float4*>(s_t + il * TP + c8 * 8 + 4);
+        val[u][0] = lo.x; val[u][1] = lo.y; val[u][2] = lo.z; val[u][3] = lo.w;
+        val[u][4] = hi.x; val[u][5] = hi.y; val[u][6] = hi.z; val[u][7] = hi.w;
+    }
+
+    // The correction for ranks [k_lo, k_hi): this workgroup's share.
+    const int rs = (r + ksplit - 1) / ksplit;
+    const int k_lo = q * rs < r ? q * rs : r;
+    const int k_hi = k_lo + rs < r ? k_lo + rs : r;
+    for (int g0 = k_lo; g0 < k_hi; g0 += kLinRG) {
+        const int gn = k_hi - g0 < kLinRG ? k_hi - g0 : kLinRG;
+        __syncthreads();  // s_aid written; s_v free (previous pass done)
+        for (int e = tid; e < BM * gn; e += kLinThreads) {
+            const int il = e / gn, kk = e - il * gn;
+            float sum = 0.f;
+            if (s_aid[il] >= 0) {
+                const float* p = vpart + (long long)(m0 + il) * r + g0 + kk;
+                for (int c = 0; c < vsplit; ++c) sum += p[(long long)c * vstride];
+            }
+            s_v[il * kLinRG + kk] = sum;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kPieces; ++u) {
+            const int pid = tid + u * kLinThreads;
+            const int il = pid / (BN / 8), c8 = pid % (BN / 8);
+            const int a = s_aid[il];
+            const int col = n0 + c8 * 8;
+            if (a < 0 || col >= H2) continue;
+            const typename DT::storage* bp = B_stack + ((long long)a * r + g0) * H2 + col;
+            float ls[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            for (int kk = 0; kk < gn; ++kk) {
+                float bv[8];
+                DT::unpack(load16(bp + (long long)kk * H2), bv);
+                const float vk = s_v[il * kLinRG + kk];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) ls[j] = fmaf(vk, bv[j], ls[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) val[u][j] = fmaf(scale, ls[j], val[u][j]);
+        }
+    }
+
+    // ---- combine the K ranges, add the bias, round, store ------------------
+    // A partial tile is stored as 8 planes of BM * BN / 8 floats, plane j
+    // holding column j of every piece, so that each store and load
+    // instruction of a wave covers consecutive words.
+    constexpr int kPlane = BM * BN / 8;
+    const long long tile_floats = (long long)BM * BN;
+    if (ksplit > 1) {
+        float* mine = part + ((long long)t * ksplit + q) * tile_floats;
+#pragma unroll
+        for (int u = 0; u < kPieces; ++u) {
+            const int pid = tid + u * kLinThreads;
+            const int il = pid / (BN / 8), c8 = pid % (BN / 8);
+            if (m0 + il >= M || n0 + c8 * 8 >= H2) continue;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) store_partial(mine + j * kPlane + pid, val[u][j]);
+        }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();  // every wave's partial stores have completed
+        if (tid == 0) {
+            int* cnt = counters + (long long)t * counter_stride;
+            const int before =
+                __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int last = before == ksplit - 1;
+            if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            *s_last = last;
+        }
+        __syncthreads();
+        if (!*s_last) return;
+        const float* tp = part + (long long)t * ksplit * tile_floats;
+#pragma unroll
+        for (int u = 0; u < kPieces; ++u) {
+            const int pid = tid + u * kLinThreads;
+            const int il = pid / (BN / 8), c8 = pid % (BN / 8);
+            if (m0 + il >= M || n0 + c8 * 8 >= H2) continue;
+            float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            for (int c = 0; c < ksplit; ++c) {
+                if (c == q) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) sum[j] += val[u][j];
+                } else {
+                    float* p = const_cast<float*>(tp) + c * tile_floats + pid;
+                    float pv[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        pv[j] = __hip_atomic_load(p + j * kPlane, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) sum[j] += pv[j];
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) val[u][j] = sum[j];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kPieces; ++u) {
+        const int pid = tid + u * kLinThreads;
+        const int il = pid / (BN / 8), c8 = pid % (BN / 8);
+        const int row = m0 + il, col = n0 + c8 * 8;
+        if (row >= M || col >= H2) continue;
+        if (bias) {
+            float bv[8];
+            DT::unpack(load16(bias + col), bv);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) val[u][j] += bv[j];
+        }
+        store16(y + (long long)row * H2 + col, DT::pack(val[u]));
+    }
+}
+
 // Grid: tiles * ksplit workgroups (rounded up; the extra ones return at
 // once), workgroup b taking K range q = b % ksplit of tile b / ksplit.  With
 // ksplit a multiple of the 8 XCDs, which receive workgroups round-robin,
@@ -250,15 +402,6 @@ __global__ __launch_bounds__(kLinThreads) void linear_lora_kernel(
     }
     __syncthreads();  // every wave is done with the staging buffers
 
-    // Adapter of each tile row.
-    for (int i = tid; i < BM; i += kLinThreads) {
-        int a = -1;
-        if (m0 + i < M)
-            a = seg_lds ? row_adapter((const int*)s_seg, (const int*)s_ids, S, m0 + i, num_adapters)
-                        : row_adapter(seg_indptr, adapter_ids, S, m0 + i, num_adapters);
-        s_aid[i] = a;
-    }
-
     // ---- accumulators -> float tile in LDS -------------------------------
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -267,127 +410,11 @@ __global__ __launch_bounds__(kLinThreads) void linear_lora_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 s_t[(wr0 + 16 * i + 4 * lg + e) * TP + wc0 + 16 * j + lr] = acc[i][j][e];
-    __syncthreads();
 
-    // ---- epilogue: row-contiguous pieces of 8 columns --------------------
-    float val[SH::kPieces][8];
-#pragma unroll
-    for (int u = 0; u < SH::kPieces; ++u) {
-        const int pid = tid + u * kLinThreads;
-        const int il = pid / (BN / 8), c8 = pid % (BN / 8);
-        const float4 lo = *reinterpret_cast<const float4*>(s_t + il * TP + c8 * 8);
-        const float4 hi = *reinterpret_cast<const float4*>(s_t + il * TP + c8 * 8 + 4);
-        val[u][0] = lo.x; val[u][1] = lo.y; val[u][2] = lo.z; val[u][3] = lo.w;
-        val[u][4] = hi.x; val[u][5] = hi.y; val[u][6] = hi.z; val[u][7] = hi.w;
-    }
-
-    // The correction for ranks [k_lo, k_hi): this workgroup's share.
-    const int rs = (r + ksplit - 1) / ksplit;
-    const int k_lo = q * rs < r ? q * rs : r;
-    const int k_hi = k_lo + rs < r ? k_lo + rs : r;
-    for (int g0 = k_lo; g0 < k_hi; g0 += kLinRG) {
-        const int gn = k_hi - g0 < kLinRG ? k_hi - g0 : kLinRG;
-        __syncthreads();  // s_aid written; s_v free (previous pass done)
-        for (int e = tid; e < BM * gn; e += kLinThreads) {
-            const int il = e / gn, kk = e - il * gn;
-            float sum = 0.f;
-            if (s_aid[il] >= 0) {
-                const float* p = vpart + (long long)(m0 + il) * r + g0 + kk;
-                for (int c = 0; c < vsplit; ++c) sum += p[(long long)c * vstride];
-            }
-            s_v[il * kLinRG + kk] = sum;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int u = 0; u < SH::kPieces; ++u) {
-            const int pid = tid + u * kLinThreads;
-            const int il = pid / (BN / 8), c8 = pid % (BN / 8);
-            const int a = s_aid[il];
-            const int col = n0 + c8 * 8;
-            if (a < 0 || col >= H2) continue;
-            const typename DT::storage* bp = B_stack + ((long long)a * r + g0) * H2 + col;
-            float ls[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            for (int kk = 0; kk < gn; ++kk) {
-                float bv[8];
-                DT::unpack(load16(bp + (long long)kk * H2), bv);
-                const float vk = s_v[il * kLinRG + kk];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) ls[j] = fmaf(vk, bv[j], ls[j]);
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) val[u][j] = fmaf(scale, ls[j], val[u][j]);
-        }
-    }
-
-    // ---- combine the K ranges, add the bias, round, store ------------------
-    // A partial tile is stored as 8 planes of BM * BN / 8 floats, plane j
-    // holding column j of every piece, so that each store and load
-    // instruction of a wave covers consecutive words.
-    constexpr int kPlane = BM * BN / 8;
-    const long long tile_floats = (long long)BM * BN;
-    if (ksplit > 1) {
-        float* mine = part + ((long long)t * ksplit + q) * tile_floats;
-#pragma unroll
-        for (int u = 0; u < SH::kPieces; ++u) {
-            const int pid = tid + u * kLinThreads;
-            const int il = pid / (BN / 8), c8 = pid % (BN / 8);
-            if (m0 + il >= M || n0 + c8 * 8 >= H2) continue;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) store_partial(mine + j * kPlane + pid, val[u][j]);
-        }
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();  // every wave's partial stores have completed
-        if (tid == 0) {
-            int* cnt = counters + (long long)t * counter_stride;
-            const int before =
-                __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const int last = before == ksplit - 1;
-            if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            s_last = last;
-        }
-        __syncthreads();
-        if (!s_last) return;
-        const float* tp = part + (long long)t * ksplit * tile_floats;
-#pragma unroll
-        for (int u = 0; u < SH::kPieces; ++u) {
-            const int pid = tid + u * kLinThreads;
-            const int il = pid / (BN / 8), c8 = pid % (BN / 8);
-            if (m0 + il >= M || n0 + c8 * 8 >= H2) continue;
-            float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            for (int c = 0; c < ksplit; ++c) {
-                if (c == q) {
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) sum[j] += val[u][j];
-                } else {
-                    float* p = const_cast<float*>(tp) + c * tile_floats + pid;
-                    float pv[8];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        pv[j] = __hip_atomic_load(p + j * kPlane, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) sum[j] += pv[j];
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) val[u][j] = sum[j];
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < SH::kPieces; ++u) {
-        const int pid = tid + u * kLinThreads;
-        const int il = pid / (BN / 8), c8 = pid % (BN / 8);
-        const int row = m0 + il, col = n0 + c8 * 8;
-        if (row >= M || col >= H2) continue;
-        if (bias) {
-            float bv[8];
-            DT::unpack(load16(bias + col), bv);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) val[u][j] += bv[j];
-        }
-        store16(y + (long long)row * H2 + col, DT::pack(val[u]));
-    }
+    linear_finish<DT, BM, BN, TP>(s_t, s_aid, s_v, s_seg, s_ids, &s_last, seg_lds, y, bias, B_stack,
+                                  vpart, vstride, vsplit, seg_indptr, adapter_ids, S, M,
+                                  num_adapters, H2, r, scale, part, counters, counter_stride,
+                                  ksplit, q, t, m0, n0);
 }
 
 // Any shape and dtype: one thread per output element, the base product as
