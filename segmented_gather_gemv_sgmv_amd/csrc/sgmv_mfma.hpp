@@ -18,14 +18,16 @@
 //
 // Shrink: X is the A operand, loaded straight from global memory (8
 // consecutive h of one row = 16 bytes).  A_a is stored [h][r] (r fastest),
-// so the B operand (8 consecutive h of one column) is gathered from an LDS
-// copy of the chunk.  The four waves split the chunk's h range and their
-// 16 x r results are summed in LDS in a fixed order.
+// so the B operand (8 consecutive h of one column) is read from an LDS copy
+// of the chunk with transposing LDS reads.  The four waves split the
+// chunk's h range and their 16 x r results are summed in LDS in a fixed
+// order.
 //
 // Expand: computed as Y^T = B^T V^T so that each lane's result is 4
-// consecutive columns of one row (one 8-byte y access).  B^T is gathered
-// from an LDS copy of the B chunk.  V is float32; to feed it to a 16-bit
-// MFMA without losing precision it is split as v = hi + lo (both 16-bit)
+// consecutive columns of one row (one 8-byte y access).  B^T is read from
+// an LDS copy of the B chunk with transposing LDS reads.  V is float32; to
+// feed it to a 16-bit MFMA without losing precision it is split as
+// v = hi + lo (both 16-bit)
 // and the K dimension is [hi | lo] against [B ; B], which keeps about 22
 // (fp16) or 16 (bf16) significant bits of v.  For fp16 the tile's v is first
 // scaled by a power of two so that max |v| lies in [2^12, 2^13) (exact,
@@ -69,11 +71,35 @@ struct MfmaOps<BF16> {
 __device__ __forceinline__ uint2 load8(const void* p) { return *reinterpret_cast<const uint2*>(p); }
 __device__ __forceinline__ void store8(void* p, const uint2& v) { *reinterpret_cast<uint2*>(p) = v; }
 
-// Packs eight 16-bit values into the 16 bytes of an MFMA operand.
-__device__ __forceinline__ uint4 pack8(const uint32_t (&h)[8]) {
-    return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                      h[6] | (h[7] << 16));
+// One MFMA operand (8 consecutive K of one row or column) gathered from a
+// tile in LDS whose rows run along the other index, with two transposing
+// LDS reads (ds_read_b64_tr_b16).  Within each group of 16 lanes, that
+// instruction gives lane i element i % 4 of the 8-byte pieces addressed by
+// lanes i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4 of the group (checked on
+// the device).  So if lane (grp, m) of the wave passes, for its group, the
+// rows k0 .. k0 + 7 of the tile (k0 uniform over the group) as
+//     row(c) = base + (k0 + m / 4 + 4 c) * ld + 4 (m % 4),  c = 0, 1,
+// it receives tile[k0 + j][m] for j = 0..7, i.e. the 16 columns starting at
+// `base` become the operand's 16 lanes.  base and ld must keep every row
+// piece 8-byte aligned.
+__device__ __forceinline__ uint4 lds_operand_tr(const uint16_t* base, int k0, int ld, int m) {
+#if __HIP_DEVICE_COMPILE__
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4s lds_v4s;
+    typedef __attribute__((address_space(3))) short lds_short;
+    const uint16_t* p0 = base + (k0 + (m >> 2)) * ld + 4 * (m & 3);
+    const uint16_t* p1 = p0 + 4 * ld;
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(lds_short*)(p0));
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(lds_short*)(p1));
+    const uint2 a = __builtin_bit_cast(uint2, lo);
+    const uint2 b = __builtin_bit_cast(uint2, hi);
+    return make_uint4(a.x, a.y, b.x, b.y);
+#else
+    (void)base; (void)k0; (void)ld; (void)m;
+    return make_uint4(0, 0, 0, 0);
+#endif
 }
+
 
 template <int R>
 struct MfmaShape {
@@ -92,7 +118,11 @@ struct MfmaShape {
     // 8-byte group g of row i sits at position g ^ (i & 15), so that neither
     // the row-piece accesses nor the MFMA-layout ones meet bank conflicts.
     static constexpr int kYU = (2 * kCW + kNT - 1) / kNT;
-    static constexpr int kStageB = R * kCW;  // LDS of the B chunk, in 16-bit units
+    // The B chunk in LDS: R rows of kCW columns, each row padded by 16
+    // elements so that the four rows one transposing read touches fall in
+    // different banks.
+    static constexpr int kLdB = kCW + 16;
+    static constexpr int kStageB = R * kLdB;  // LDS of the B chunk, in 16-bit units
     static_assert(kStageB >= kT * kCW, "the y tile must fit over the B chunk");
     static_assert(kCW % 64 == 0, "the swizzle needs at least 16 groups per row");
     static_assert(kBV * kNT * 8 == R * kCW, "B chunk must split evenly over the threads");
@@ -153,13 +183,15 @@ __device__ __forceinline__ void shrink_chunk_mfma(const typename DT::storage* __
     for (int s = 0; s < Sh::kXSteps; ++s) {
         const int hl = wid * kq + s * 32 + grp * 8;
         if (s * 32 < kq) {  // wave-uniform
+            // Rows hl .. hl + 7 of the chunk are all inside it or all past it
+            // (both are multiples of 8); past it, LDS holds no data of this
+            // chunk, so the operand is zeroed.
+            const bool in = hl < kc;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                uint32_t hb[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    hb[j] = hl < kc ? (uint32_t)s_a[(hl + j) * R + nb * 16 + m] : 0u;
-                acc[nb] = Ops::mma(xa[s], pack8(hb), acc[nb]);
+                uint4 hb = lds_operand_tr(s_a + nb * 16, hl, R, m);
+                if (!in) hb = make_uint4(0, 0, 0, 0);
+                acc[nb] = Ops::mma(xa[s], hb, acc[nb]);
             }
         }
     }
@@ -241,7 +273,7 @@ __device__ __forceinline__ void expand_apply(const ExpandRegs<R>& e, uint16_t* s
 #pragma unroll
     for (int u = 0; u < Sh::kBV; ++u) {
         const int t = tid + u * NT;
-        store16(s_b + (t / (CW / 8)) * CW + (t % (CW / 8)) * 8, e.bq[u]);
+        store16(s_b + (t / (CW / 8)) * Sh::kLdB + (t % (CW / 8)) * 8, e.bq[u]);
     }
     // The largest |v| of the tile for the fp16 range scaling.
     int shift = 0;
@@ -278,14 +310,12 @@ __device__ __forceinline__ void expand_apply(const ExpandRegs<R>& e, uint16_t* s
         acc[q] = mf32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 2 * R / 32; ++ks) {
-            uint32_t ab[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int kr = (ks * 32 + grp * 8 + j) % R;  // hi and lo both meet B row kr
-                ab[j] = s_b[kr * CW + cb * 16 + m];
-            }
+            // B rows kr .. kr + 7 (hi and lo both meet B row kr), columns
+            // cb * 16 + [0, 16).
+            const int kr = (ks * 32 + grp * 8) % R;
+            const uint4 ab = lds_operand_tr(s_b + cb * 16, kr, Sh::kLdB, m);
             const uint4 bv = *reinterpret_cast<const uint4*>(s_vh + m * 2 * R + ks * 32 + grp * 8);
-            acc[q] = Ops::mma(pack8(ab), bv, acc[q]);
+            acc[q] = Ops::mma(ab, bv, acc[q]);
         }
     }
     // The y tile, as loaded (row pieces), into LDS over the B chunk: every
