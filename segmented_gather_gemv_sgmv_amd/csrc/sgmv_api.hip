@@ -231,6 +231,17 @@ MfmaSplitPlan make_mfma_split_plan(const MfmaPlan& mp, int H1, int H2, int r) {
     long long hps = (H1 + k - 1) / k;
     hps = (hps + 127) / 128 * 128;
     if (hps > kc_max) hps = kc_max;
+    // Large ranks have small LDS chunks, and one workgroup (with one
+    // float32 partial of the tile's v) per chunk multiplies the partials:
+    // at r = 128 and H1 = 4096, 32 chunks write and re-read 16 KB per row,
+    // twice the row of x.  Where the partials are heavy (chunks x rank >
+    // 256), a workgroup takes as many chunks as keep the launch near one
+    // round of workgroups; for small ranks, more workgroups in flight pay
+    // more than the partials cost.
+    if (k * r > 256 && sp.slots * k > 2LL * kTargetWorkgroups) {
+        const long long cpw = (sp.slots * k + kTargetWorkgroups - 1) / kTargetWorkgroups;
+        hps = cpw * kc_max;
+    }
     sp.h_per_split = (int)hps;
     sp.ksplit = (int)((H1 + hps - 1) / hps);
     sp.grid_shrink = sp.slots * sp.ksplit;

@@ -493,12 +493,21 @@ __global__ __launch_bounds__(256) void shrink_mfma_kernel(
                 : locate_tile<NT>(seg_indptr, adapter_ids, S, num_rows, num_adapters, T, g, s_scan,
                                   tile);
     if (!have) return;
+    // The workgroup's H1 range, in LDS-sized chunks summed in order: the
+    // first chunk stores the partial, later ones add to it (each value is
+    // read back by the thread that stored it).
     const int h_lo = p * h_per_split;
     const int h_hi = min(H1, h_lo + h_per_split);
     float* out = partials + (long long)p * num_rows * R + (long long)tile.row0 * R;
-    shrink_chunk_mfma<DT, R>(A_stack + (long long)tile.adapter * H1 * R,
-                             x + (long long)tile.row0 * H1, tile.nrows, H1, h_lo, h_hi, s_a, s_red,
-                             [&](int i, int k, float v) { out[i * R + k] = v; });
+    for (int c_lo = h_lo; c_lo < h_hi; c_lo += Sh::kKcMax) {
+        const bool first = c_lo == h_lo;
+        shrink_chunk_mfma<DT, R>(A_stack + (long long)tile.adapter * H1 * R,
+                                 x + (long long)tile.row0 * H1, tile.nrows, H1, c_lo,
+                                 min(h_hi, c_lo + Sh::kKcMax), s_a, s_red,
+                                 [&](int i, int k, float v) {
+                                     out[i * R + k] = first ? v : out[i * R + k] + v;
+                                 });
+    }
 }
 
 template <typename DT, int R>

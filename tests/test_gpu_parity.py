@@ -302,6 +302,10 @@ def test_workspace_reused_across_shapes():
 @pytest.mark.parametrize("seed,dtype,H1,H2,r,N,R,S,tail", [
     (41, "bf16", 1024, 3072, 64, 7, 3000, 5, 0),
     (42, "f16", 512, 1024, 128, 4, 2000, 3, 37),
+    # more than two rounds of one-chunk workgroups: each shrink workgroup
+    # sums several LDS-sized chunks (ragged last range)
+    (43, "f16", 2048, 1024, 128, 6, 2400, 4, 19),
+    (44, "bf16", 4096, 1024, 64, 9, 2048, 8, 0),
 ])
 def test_two_launch_mfma_path(seed, dtype, H1, H2, r, N, R, S, tail):
     """Row-heavy calls too large for one resident round of single-kernel
