@@ -457,7 +457,7 @@ bool grid_fits(const Plan& p, int H2) {
 // columns of output).
 using LinSkinny = LinearShape<1, 4, 4, 1, 4>;
 using LinSquare = LinearShape<2, 2, 4, 4, 2>;
-constexpr int kLinTargetWorkgroups = 512;  // split K until the grid has this many
+constexpr int kLinTargetWorkgroups = 256;  // split K until the grid has this many
 
 struct LinearPlan {
     int cfg;  // 0 skinny tiles, 1 square tiles, -1 the element-wise kernel

@@ -100,6 +100,46 @@ __device__ __forceinline__ int row_adapter(P seg_indptr, P adapter_ids, int S, i
     return (a >= 0 && a < num_adapters) ? a : -1;
 }
 
+// Ranks [k_lo, k_hi) of the correction handled by K range q of ksplit.
+__device__ __forceinline__ void linear_rank_share(int r, int ksplit, int q, int& k_lo, int& k_hi) {
+    const int rs = (r + ksplit - 1) / ksplit;
+    k_lo = q * rs < r ? q * rs : r;
+    k_hi = k_lo + rs < r ? k_lo + rs : r;
+}
+
+// What the correction needs that does not depend on the base product, done
+// before the main loop so that its round trips overlap the first chunks'
+// loads: each tile row's adapter (s_aid) and the first pass of v (the
+// workgroup's first kLinRG ranks, s_v, summed over the shrink's chunks in
+// order).  v is summed for every row below M; rows without an adapter
+// never use theirs.  The caller must make s_seg / s_ids visible first and
+// synchronise before s_aid / s_v are read.
+__device__ __forceinline__ void linear_prepare(int* s_aid, float* s_v, const int* s_seg,
+                                               const int* s_ids, bool seg_lds,
+                                               const float* __restrict__ vpart, long long vstride,
+                                               int vsplit, const int* __restrict__ seg_indptr,
+                                               const int* __restrict__ adapter_ids, int S, int M,
+                                               int num_adapters, int r, int ksplit, int q, int m0,
+                                               int BM) {
+    const int tid = threadIdx.x;
+    for (int i = tid; i < BM; i += kLinThreads) {
+        int a = -1;
+        if (m0 + i < M)
+            a = seg_lds ? row_adapter((const int*)s_seg, (const int*)s_ids, S, m0 + i, num_adapters)
+                        : row_adapter(seg_indptr, adapter_ids, S, m0 + i, num_adapters);
+        s_aid[i] = a;
+    }
+    int k_lo, k_hi;
+    linear_rank_share(r, ksplit, q, k_lo, k_hi);
+    const int gn = k_hi - k_lo < kLinRG ? k_hi - k_lo : kLinRG;
+    for (int e = tid; e < BM * gn; e += kLinThreads) {
+        const int il = e / gn, kk = e - il * gn;
+        s_v[il * kLinRG + kk] =
+            m0 + il < M ? sum_partials(vpart + (long long)(m0 + il) * r + k_lo + kk, vstride, vsplit)
+                        : 0.f;
+    }
+}
+
 // The part of an adapted-linear tile that follows the base product, shared
 // by the tile kernels.  On entry s_t holds the tile's float32 base product
 // for this workgroup's K range ([BM][TP], written by the caller; the barrier
@@ -120,16 +160,7 @@ __device__ __forceinline__ void linear_finish(
     constexpr int kPieces = BM * BN / 8 / kLinThreads;
     static_assert(BM * BN % (8 * kLinThreads) == 0, "uneven epilogue");
     const int tid = threadIdx.x;
-    // Adapter of each tile row.
-    for (int i = tid; i < BM; i += kLinThreads) {
-        int a = -1;
-        if (m0 + i < M)
-            a = seg_lds ? row_adapter((const int*)s_seg, (const int*)s_ids, S, m0 + i, num_adapters)
-                        : row_adapter(seg_indptr, adapter_ids, S, m0 + i, num_adapters);
-        s_aid[i] = a;
-    }
-
-    __syncthreads();  // s_aid, and the caller's s_t
+    __syncthreads();  // the caller's s_t (s_aid and the first s_v are older)
 
     // ---- epilogue: row-contiguous pieces of 8 columns --------------------
     float val[kPieces][8];
@@ -143,23 +174,26 @@ __device__ __forceinline__ void linear_finish(
         val[u][4] = hi.x; val[u][5] = hi.y; val[u][6] = hi.z; val[u][7] = hi.w;
     }
 
-    // The correction for ranks [k_lo, k_hi): this workgroup's share.
-    const int rs = (r + ksplit - 1) / ksplit;
-    const int k_lo = q * rs < r ? q * rs : r;
-    const int k_hi = k_lo + rs < r ? k_lo + rs : r;
+    // The correction for ranks [k_lo, k_hi): this workgroup's share.  The
+    // first pass's v came from linear_prepare; later passes (shares above
+    // kLinRG ranks) sum theirs here.
+    int k_lo, k_hi;
+    linear_rank_share(r, ksplit, q, k_lo, k_hi);
     for (int g0 = k_lo; g0 < k_hi; g0 += kLinRG) {
         const int gn = k_hi - g0 < kLinRG ? k_hi - g0 : kLinRG;
-        __syncthreads();  // s_aid written; s_v free (previous pass done)
-        for (int e = tid; e < BM * gn; e += kLinThreads) {
-            const int il = e / gn, kk = e - il * gn;
-            float sum = 0.f;
-            if (s_aid[il] >= 0) {
-                const float* p = vpart + (long long)(m0 + il) * r + g0 + kk;
-                for (int c = 0; c < vsplit; ++c) sum += p[(long long)c * vstride];
+        if (g0 > k_lo) {
+            __syncthreads();  // s_v free (previous pass done)
+            for (int e = tid; e < BM * gn; e += kLinThreads) {
+                const int il = e / gn, kk = e - il * gn;
+                float sum = 0.f;
+                if (s_aid[il] >= 0) {
+                    // chunk order, eight loads in flight
+                    sum = sum_partials(vpart + (long long)(m0 + il) * r + g0 + kk, vstride, vsplit);
+                }
+                s_v[il * kLinRG + kk] = sum;
             }
-            s_v[il * kLinRG + kk] = sum;
+            __syncthreads();
         }
-        __syncthreads();
 #pragma unroll
         for (int u = 0; u < kPieces; ++u) {
             const int pid = tid + u * kLinThreads;
@@ -169,12 +203,23 @@ __device__ __forceinline__ void linear_finish(
             if (a < 0 || col >= H2) continue;
             const typename DT::storage* bp = B_stack + ((long long)a * r + g0) * H2 + col;
             float ls[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            for (int kk = 0; kk < gn; ++kk) {
-                float bv[8];
-                DT::unpack(load16(bp + (long long)kk * H2), bv);
-                const float vk = s_v[il * kLinRG + kk];
+            // ranks in order, four B rows in flight at a time
+            for (int k0 = 0; k0 < gn; k0 += 4) {
+                uint4 braw[4];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) ls[j] = fmaf(vk, bv[j], ls[j]);
+                for (int d = 0; d < 4; ++d)
+                    braw[d] = k0 + d < gn ? load16(bp + (long long)(k0 + d) * H2)
+                                          : make_uint4(0, 0, 0, 0);
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    if (k0 + d < gn) {
+                        float bv[8];
+                        DT::unpack(braw[d], bv);
+                        const float vk = s_v[il * kLinRG + k0 + d];
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) ls[j] = fmaf(vk, bv[j], ls[j]);
+                    }
+                }
             }
 #pragma unroll
             for (int j = 0; j < 8; ++j) val[u][j] = fmaf(scale, ls[j], val[u][j]);
@@ -217,20 +262,27 @@ __device__ __forceinline__ void linear_finish(
             const int il = pid / (BN / 8), c8 = pid % (BN / 8);
             if (m0 + il >= M || n0 + c8 * 8 >= H2) continue;
             float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            for (int c = 0; c < ksplit; ++c) {
-                if (c == q) {
+            // K ranges in order, the other ranges' partials four at a time
+            // with all their loads in flight (one round trip per four).
+            for (int c0 = 0; c0 < ksplit; c0 += 4) {
+                float pv[4][8];
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) sum[j] += val[u][j];
-                } else {
+                for (int d = 0; d < 4; ++d) {
+                    const int c = c0 + d;
                     float* p = const_cast<float*>(tp) + c * tile_floats + pid;
-                    float pv[8];
 #pragma unroll
                     for (int j = 0; j < 8; ++j)
-                        pv[j] = __hip_atomic_load(p + j * kPlane, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) sum[j] += pv[j];
+                        pv[d][j] = (c < ksplit && c != q)
+                                       ? __hip_atomic_load(p + j * kPlane, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT)
+                                       : val[u][j];
                 }
+#pragma unroll
+                for (int d = 0; d < 4; ++d)
+                    if (c0 + d < ksplit) {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) sum[j] += pv[d][j];
+                    }
             }
 #pragma unroll
             for (int j = 0; j < 8; ++j) val[u][j] = sum[j];
@@ -380,13 +432,17 @@ __global__ __launch_bounds__(kLinThreads) void linear_lora_kernel(
     for (int d = 0; d < PD; ++d)
         if (d < nchunks) load_chunk(d, ring[d]);
 
-    // The segment table, into LDS (read in the epilogue, after barriers).
+    // The segment table, into LDS, then what the correction needs that does
+    // not depend on the base product (its loads overlap the first chunks').
 #pragma unroll
     for (int u = 0; u < kSegU; ++u) {
         const int e = tid + u * kLinThreads;
         if (seg_lds && e <= S) s_seg[e] = seg_r[u];
         if (seg_lds && e < S) s_ids[e] = ids_r[u];
     }
+    lds_barrier();
+    linear_prepare(s_aid, s_v, s_seg, s_ids, seg_lds, vpart, vstride, vsplit, seg_indptr,
+                   adapter_ids, S, M, num_adapters, r, ksplit, q, m0, BM);
 
     for (int c0 = 0; c0 < nchunks; c0 += PD) {
 #pragma unroll
