@@ -66,6 +66,7 @@ struct Plan {
     int ksplit;       // chunks of the H1 reduction
     int h_per_split;  // rows of A per chunk
     int num_segments, num_rows;
+    int rows;         // rows per tile of the vectorised shrink
 };
 
 // Pure function of the shapes (not of pointers), so that the workspace size
@@ -77,7 +78,10 @@ Plan make_plan(int num_rows, int num_segments, int H1, int r, int dtype) {
     const bool vec = vec_rank(dtype, r);
     // The split is sized with the vectorised kernel's tile height whichever
     // kernel runs, so that it stays a function of the shapes alone.
-    const long long slots = tile_slots(num_segments, num_rows, vec ? kShrinkRows : kGenericRows);
+    // One-row tiles when no segment needs more on average (decode batches):
+    // a tile's registers then hold one row's accumulators, not eight.
+    p.rows = num_rows <= num_segments ? 1 : kShrinkRows;
+    const long long slots = tile_slots(num_segments, num_rows, vec ? p.rows : kGenericRows);
 
     // Enough workgroups to fill the chip, but no chunk below kMinChunkBytes.
     const long long a_bytes = (long long)H1 * r * elem_bytes(dtype);
@@ -336,10 +340,15 @@ void launch_shrink_vec(float* out, long long out_stride, const void* x, const vo
                        const int32_t* seg, const int32_t* ids, int S, int rows, int nad, int H1,
                        const Plan& p, hipStream_t st) {
     using T = typename DT::storage;
-    const unsigned grid = (unsigned)(tile_slots(S, rows, kShrinkRows) * p.ksplit);
-    launch(&shrink_vec_kernel<DT, R, kShrinkThreads, kShrinkRows, kShrinkPG>, dim3(grid), dim3(kShrinkThreads), st, out, out_stride,
-                       (const T*)x, (const T*)A, seg, ids, S, rows, nad, H1, p.ksplit,
-                       p.h_per_split);
+    const unsigned grid = (unsigned)(tile_slots(S, rows, p.rows) * p.ksplit);
+    if (p.rows == 1)
+        launch(&shrink_vec_kernel<DT, R, kShrinkThreads, 1, kShrinkPG>, dim3(grid),
+               dim3(kShrinkThreads), st, out, out_stride, (const T*)x, (const T*)A, seg, ids, S,
+               rows, nad, H1, p.ksplit, p.h_per_split);
+    else
+        launch(&shrink_vec_kernel<DT, R, kShrinkThreads, kShrinkRows, kShrinkPG>, dim3(grid),
+               dim3(kShrinkThreads), st, out, out_stride, (const T*)x, (const T*)A, seg, ids, S,
+               rows, nad, H1, p.ksplit, p.h_per_split);
 }
 
 template <typename DT>
@@ -443,7 +452,7 @@ void with_dtype(int dtype, F&& f) {
 // Whichever kernel a call ends up on, its grid must fit one launch.  The
 // general kernels have the shortest tiles and so the most slots.
 bool grid_fits(const Plan& p, int H2) {
-    const long long slots = tile_slots(p.num_segments, p.num_rows, kGenericRows);
+    const long long slots = tile_slots(p.num_segments, p.num_rows, 1);  // the most tiles
     const long long csplit = (H2 + kGenericThreads - 1) / kGenericThreads;
     const long long csplit_vec = (H2 + kWave * 4 - 1) / (kWave * 4);
     return slots * p.ksplit <= kMaxGrid && slots * csplit <= kMaxGrid &&
