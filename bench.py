@@ -264,6 +264,46 @@ def run_linear(w, mode: str, steps: int, warmup: int, device="cuda:0"):
             "base_flops_TFLOPs": 2.0 * w.num_rows * w.H1 * w.H2 / us / 1e6}
 
 
+def copy_floor(w, steps: int, warmup: int, device="cuda:0"):
+    """What a plain device-to-device copy moving the workload's algorithmic
+    bytes per call (half read, half written) costs under the same method:
+    buffers rotated over >= 1 GiB so that every copy reads HBM, the timed
+    copies captured in one HIP graph, HIP events on the replay stream.  A
+    reference for how fast any single launch can move that many bytes cold
+    on this device; not a figure of the SGMV kernels."""
+    import torch
+    dev = torch.device(device)
+    half = max(algorithmic_bytes(w) // 2 // 16 * 16, 16)
+    nsets = max(2, min(512, math.ceil(ROTATE_BYTES / (2 * half))))
+    src = [torch.empty(half, dtype=torch.uint8, device=dev).fill_(1) for _ in range(nsets)]
+    dst = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(nsets)]
+    for i in range(warmup):
+        dst[i % nsets].copy_(src[i % nsets])
+    torch.cuda.synchronize(dev)
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        dst[0].copy_(src[0])
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize(dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for k in range(steps):
+            dst[(warmup + k) % nsets].copy_(src[(warmup + k) % nsets])
+    torch.cuda.synchronize(dev)
+    stream = torch.cuda.current_stream(dev)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    g.replay()
+    end.record(stream)
+    torch.cuda.synchronize(dev)
+    us = start.elapsed_time(end) * 1e3 / steps
+    moved = 2 * half
+    return {"mode": "copy floor", "workload": w.name, "bytes_moved_per_copy": moved,
+            "us_per_copy": us, "GBps": moved / us / 1e3, "hbm_peak_frac": moved / us / 1e3 / HBM_PEAK_GBPS,
+            "buffer_sets_rotated": nsets}
+
+
 def copy_calibration(nbytes: int, reps: int = 20):
     """A plain device-to-device copy of known size, for scaling the
     FETCH_SIZE / WRITE_SIZE counters (run it under rocprofv3 --pmc)."""
@@ -390,6 +430,9 @@ def main(argv=None):
     ap.add_argument("--linear", choices=("fused", "unfused"), default=None,
                     help="instead: time the adapted linear layer over the workload's batch, "
                          "base product fused in (lora_linear) or not (addmm + lora_apply)")
+    ap.add_argument("--floor", action="store_true",
+                    help="instead: time a plain device copy moving the workload's algorithmic "
+                         "bytes per call, cold, as a reference floor for one launch")
     ap.add_argument("--workload", default="llama7b_decode", choices=sorted(WORKLOADS),
                     help="workload to time (default: the Llama-2-7B decode projection); the "
                          "others are the remaining seeded configurations")
@@ -413,6 +456,9 @@ def main(argv=None):
     w = WORKLOADS[args.workload](wl)
     if args.adapter_load:
         print(json.dumps(adapter_load(w)), flush=True)
+        return 0
+    if args.floor:
+        print(json.dumps(copy_floor(w, args.steps, args.warmup)), flush=True)
         return 0
     if args.linear:
         print(json.dumps(run_linear(w, args.linear, args.steps, args.warmup)), flush=True)
@@ -465,6 +511,12 @@ def main(argv=None):
         },
         "wall_s_timed": res["wall_s"],
     }
+    if not args.warm:
+        # A plain copy moving the same bytes per launch, cold, same method.
+        fl = copy_floor(w, args.steps, args.warmup)
+        line["roofline"]["copy_floor"] = {"us": fl["us_per_copy"], "GBps": fl["GBps"],
+                                          "frac_of_peak": fl["hbm_peak_frac"],
+                                          "kernel_vs_floor": step_s * 1e6 / fl["us_per_copy"]}
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(line), flush=True)
