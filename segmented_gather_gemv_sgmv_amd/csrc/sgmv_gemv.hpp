@@ -138,22 +138,20 @@ __global__ __launch_bounds__(NT) void shrink_vec_kernel(
 
     const int h_lane = tid / LPR;             // row offset of this lane within a pass
     const int k0 = (tid % LPR) * VEC;         // first column of this lane
-    // With one-row tiles the x values are read together with the A pass
-    // (one round trip for both, instead of x after A); taller tiles read
-    // them as they are used, which keeps their registers down.  The FMA
-    // order is the same either way.
-    constexpr int XB = RB == 1 ? 1 : 0;
+    // With one-row tiles the x value is read together with the A pass (one
+    // round trip for both, instead of x after A); taller tiles read theirs
+    // as they are used, which keeps their registers down.  The FMA order is
+    // the same either way.
+    constexpr bool kEarlyX = RB == 1;
     for (int hb = h_lo; hb < h_hi; hb += HPB * PG) {
         uint4 av[PG];
-        float xv[PG][XB > 0 ? XB : 1];
+        float x0[PG];
 #pragma unroll
         for (int q = 0; q < PG; ++q) {
             const int h = hb + q * HPB + h_lane;
             const bool in = h < h_hi;
             av[q] = in ? load16(A + (long long)h * R + k0) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-            for (int i = 0; i < XB; ++i)
-                xv[q][i] = (in && i < nrows) ? DT::load1(xr + (long long)i * H1 + h) : 0.f;
+            x0[q] = (kEarlyX && in && nrows > 0) ? DT::load1(xr + h) : 0.f;
         }
 #pragma unroll
         for (int q = 0; q < PG; ++q) {
@@ -164,8 +162,8 @@ __global__ __launch_bounds__(NT) void shrink_vec_kernel(
 #pragma unroll
                 for (int i = 0; i < RB; ++i) {
                     if (i < nrows) {
-                        const float x1 = i < XB ? xv[q][i < XB ? i : 0]
-                                                : DT::load1(xr + (long long)i * H1 + h);
+                        const float x1 = (kEarlyX && i == 0) ? x0[q]
+                                                             : DT::load1(xr + (long long)i * H1 + h);
 #pragma unroll
                         for (int c = 0; c < VEC; ++c) acc[i * VEC + c] = fmaf(x1, af[c], acc[i * VEC + c]);
                     }
