@@ -160,7 +160,25 @@ def run_gpu(w, steps: int, warmup: int, device="cuda:0", row_ids=None, projectio
     torch.cuda.synchronize(device)
     wall = time.perf_counter() - t0
     gpu_ms = start.elapsed_time(end)
-    return dict(gpu_ms=gpu_ms, wall_s=wall, nsets=nsets, per_set_bytes=per_set)
+    # Spread: a graph of `chunk` steps (every buffer set at least once)
+    # replayed `reps` times, each replay timed on its own; the per-call means
+    # of the replays give p10 / p50 / p90.
+    chunk = max(100, nsets)
+    reps = 20
+    g2 = st.capture(chunk, first=warmup)
+    torch.cuda.synchronize(device)
+    samples = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g2.replay()
+        b.record(stream)
+        torch.cuda.synchronize(device)
+        samples.append(a.elapsed_time(b) * 1e3 / chunk)
+    pct = np.percentile(np.asarray(samples), [10, 50, 90]).tolist()
+    return dict(gpu_ms=gpu_ms, wall_s=wall, nsets=nsets, per_set_bytes=per_set,
+                us_p10_p50_p90=pct, spread_steps=chunk, spread_replays=reps)
 
 
 KERNEL_SOURCES = ("segmented_gather_gemv_sgmv_amd/csrc/sgmv_api.hip",
@@ -493,6 +511,9 @@ def main(argv=None):
                               else f"built on the device from per-row ids ({args.row_ids})"),
         },
         "us_per_call": step_s * 1e6,
+        "us_per_call_p10_p50_p90": res["us_p10_p50_p90"],
+        "spread": f"per-call means of {res['spread_replays']} separately timed replays "
+                  f"of a {res['spread_steps']}-step graph",
         "achieved_hbm_GBps": achieved,
         "hbm_peak_frac": achieved / HBM_PEAK_GBPS,
         "roofline": {
