@@ -51,6 +51,21 @@ def algorithmic_bytes(w) -> int:
     return weights + rows * w.H1 * e + 2 * rows * w.H2 * e
 
 
+def entry_bytes(w, entry: str) -> int:
+    """Algorithmic bytes of one call of an entry point: lora_apply as above;
+    sgmv_shrink reads each segment's A once and x once and writes v (float32);
+    sgmv_expand reads each segment's B once and v, and reads and writes y."""
+    if entry == "apply":
+        return algorithmic_bytes(w)
+    e = w.elem_bytes
+    lens = w.seg_lengths
+    segs = int((lens > 0).sum())
+    rows = int(lens.sum())
+    if entry == "shrink":
+        return segs * w.H1 * w.r * e + rows * w.H1 * e + rows * w.r * 4
+    return segs * w.r * w.H2 * e + rows * w.r * 4 + 2 * rows * w.H2 * e
+
+
 def algorithmic_flops(w) -> int:
     rows = int(w.seg_lengths.sum())
     return 2 * rows * w.r * (w.H1 + w.H2)
@@ -59,9 +74,11 @@ def algorithmic_flops(w) -> int:
 class BenchState:
     """Device copies of a workload, rotated over `nsets` buffer sets."""
 
-    def __init__(self, w, nsets: int, device="cuda:0", row_ids=None, projections=1):
+    def __init__(self, w, nsets: int, device="cuda:0", row_ids=None, projections=1,
+                 entry="apply"):
         import torch
         import segmented_gather_gemv_sgmv_amd as sg
+        self.entry = entry
         self.w = w
         self.sg = sg
         dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
@@ -77,6 +94,8 @@ class BenchState:
             if projections == 1:
                 s = {k: (v if i == 0 else v.clone()) for k, v in base.items() if k != "y0"}
                 s["y"] = base["y0"].clone()
+                if entry != "apply":  # float32 v [R, r] of the separate entry points
+                    s["v"] = torch.randn(w.num_rows, w.r, device=dev) * 0.5
             else:  # one copy of the shape per projection
                 s = {k: [v.clone() for _ in range(projections)] for k, v in base.items()
                      if k != "y0"}
@@ -84,6 +103,7 @@ class BenchState:
             self.sets.append(s)
         self.y0 = base["y0"]
         nbytes = sg.lora_apply_workspace_bytes(w.num_rows, w.num_segments, w.H1, w.H2, w.r, dt)
+        nbytes = max(nbytes, sg.shrink_workspace_bytes(w.num_rows, w.num_segments, w.H1, w.r, dt))
         if projections > 1:
             nbytes = max(nbytes, sg.lora_apply_multi_workspace_bytes(
                 [(w.H1, w.H2)] * projections, w.num_rows, w.num_segments, w.r, dt))
@@ -115,6 +135,12 @@ class BenchState:
                 [(s["y"][p], s["x"][p], s["A"][p], s["B"][p], self.w.scale)
                  for p in range(self.projections)], seg, ids, workspace=self.workspace)
             return
+        if self.entry == "shrink":
+            self.sg.sgmv_shrink(s["v"], s["x"], s["A"], seg, ids, workspace=self.workspace)
+            return
+        if self.entry == "expand":
+            self.sg.sgmv_expand(s["y"], s["v"], s["B"], seg, ids, self.w.scale)
+            return
         self.sg.lora_apply(s["y"], s["x"], s["A"], s["B"], seg, ids, self.w.scale,
                            workspace=self.workspace)
 
@@ -140,11 +166,11 @@ class BenchState:
 
 
 def run_gpu(w, steps: int, warmup: int, device="cuda:0", row_ids=None, projections=1,
-            warm=False):
+            warm=False, entry="apply"):
     import torch
     per_set = (w.x.size + w.A.size + w.B.size + w.y0.size) * w.elem_bytes * projections
     nsets = 1 if warm else max(1, min(512, math.ceil(ROTATE_BYTES / max(per_set, 1))))
-    st = BenchState(w, nsets, device, row_ids, projections)
+    st = BenchState(w, nsets, device, row_ids, projections, entry)
     for i in range(warmup):
         st.step(i)
     torch.cuda.synchronize(device)
@@ -282,7 +308,7 @@ def run_linear(w, mode: str, steps: int, warmup: int, device="cuda:0"):
             "base_flops_TFLOPs": 2.0 * w.num_rows * w.H1 * w.H2 / us / 1e6}
 
 
-def copy_floor(w, steps: int, warmup: int, device="cuda:0"):
+def copy_floor(w, steps: int, warmup: int, device="cuda:0", nbytes=None):
     """What a plain device-to-device copy moving the workload's algorithmic
     bytes per call (half read, half written) costs under the same method:
     buffers rotated over >= 1 GiB so that every copy reads HBM, the timed
@@ -291,7 +317,7 @@ def copy_floor(w, steps: int, warmup: int, device="cuda:0"):
     on this device; not a figure of the SGMV kernels."""
     import torch
     dev = torch.device(device)
-    half = max(algorithmic_bytes(w) // 2 // 16 * 16, 16)
+    half = max((algorithmic_bytes(w) if nbytes is None else nbytes) // 2 // 16 * 16, 16)
     nsets = max(2, min(512, math.ceil(ROTATE_BYTES / (2 * half))))
     src = [torch.empty(half, dtype=torch.uint8, device=dev).fill_(1) for _ in range(nsets)]
     dst = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(nsets)]
@@ -448,6 +474,9 @@ def main(argv=None):
     ap.add_argument("--linear", choices=("fused", "unfused"), default=None,
                     help="instead: time the adapted linear layer over the workload's batch, "
                          "base product fused in (lora_linear) or not (addmm + lora_apply)")
+    ap.add_argument("--entry", choices=("apply", "shrink", "expand"), default="apply",
+                    help="entry point timed: lora_apply (default), or sgmv_shrink / sgmv_expand "
+                         "alone, each against its own algorithmic bytes")
     ap.add_argument("--floor", action="store_true",
                     help="instead: time a plain device copy moving the workload's algorithmic "
                          "bytes per call, cold, as a reference floor for one launch")
@@ -482,11 +511,21 @@ def main(argv=None):
         print(json.dumps(run_linear(w, args.linear, args.steps, args.warmup)), flush=True)
         return 0
     P = args.projections
-    res = run_gpu(w, args.steps, args.warmup, row_ids=args.row_ids, projections=P, warm=args.warm)
+    entry = args.entry
+    if entry != "apply" and (P != 1 or args.row_ids):
+        print("bench.py: --entry shrink|expand times one add-on with a given segment table",
+              file=sys.stderr)
+        return 2
+    res = run_gpu(w, args.steps, args.warmup, row_ids=args.row_ids, projections=P, warm=args.warm,
+                  entry=entry)
     step_s = res["gpu_ms"] / 1e3 / args.steps
     rows = int(w.seg_lengths.sum()) * P  # a row through one add-on is one SGMV row
-    abytes = algorithmic_bytes(w) * P
+    abytes = entry_bytes(w, entry) * P
     flops = algorithmic_flops(w) * P
+    if entry == "shrink":
+        flops = 2 * rows * w.r * w.H1
+    elif entry == "expand":
+        flops = 2 * rows * w.r * w.H2
     achieved = abytes / step_s / 1e9
     line = {
         "metric": "SGMV rows/s and achieved HBM GB/s (% of peak) per layer call, H=4096 r=16",
@@ -509,6 +548,8 @@ def main(argv=None):
             "cache": "warm (inputs reused every step)" if args.warm else "cold (rotated buffers)",
             "segment_table": ("given" if args.row_ids is None
                               else f"built on the device from per-row ids ({args.row_ids})"),
+            "entry_point": {"apply": "lora_apply", "shrink": "sgmv_shrink",
+                            "expand": "sgmv_expand"}[entry],
         },
         "us_per_call": step_s * 1e6,
         "us_per_call_p10_p50_p90": res["us_p10_p50_p90"],
@@ -520,13 +561,14 @@ def main(argv=None):
             "bound": "hbm",
             "kernel": ("lora_fused_kernel (one launch per step)"
                        if args.workload == "llama7b_decode" and args.row_ids is None and P == 1
-                       else "every launch of one step"),
+                       and entry == "apply" else "every launch of one step"),
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": (measured_traffic(w.name)
-                        if args.row_ids is None and P == 1 and not args.warm else None),
+                        if args.row_ids is None and P == 1 and not args.warm and entry == "apply"
+                        else None),
             "algorithmic_bytes_per_launch": abytes,
             "tflops": flops / step_s / 1e12,
         },
@@ -534,7 +576,7 @@ def main(argv=None):
     }
     if not args.warm:
         # A plain copy moving the same bytes per launch, cold, same method.
-        fl = copy_floor(w, args.steps, args.warmup)
+        fl = copy_floor(w, args.steps, args.warmup, nbytes=abytes)
         line["roofline"]["copy_floor"] = {"us": fl["us_per_copy"], "GBps": fl["GBps"],
                                           "frac_of_peak": fl["hbm_peak_frac"],
                                           "kernel_vs_floor": step_s * 1e6 / fl["us_per_copy"]}

@@ -254,6 +254,22 @@ MfmaSplitPlan make_mfma_split_plan(const MfmaPlan& mp, int H1, int H2, int r) {
     return sp;
 }
 
+// Calls f(DT{}, integral_constant<R>) for the MFMA tile kernels' dtypes
+// (fp16, bf16) and ranks (16, 32, 64, 128); the caller has checked both.
+template <typename F>
+void with_mfma_rank(int dtype, int r, F&& f) {
+    auto by_rank = [&](auto dt) {
+        switch (r) {
+            case 16: f(dt, std::integral_constant<int, 16>{}); break;
+            case 32: f(dt, std::integral_constant<int, 32>{}); break;
+            case 64: f(dt, std::integral_constant<int, 64>{}); break;
+            default: f(dt, std::integral_constant<int, 128>{}); break;
+        }
+    };
+    if (dtype == SGMV_F16) by_rank(F16{});
+    else by_rank(BF16{});
+}
+
 bool use_mfma(int num_rows, int num_segments) {
     return (long long)num_rows >= (long long)kMfmaRowsPerSegment * num_segments;
 }
@@ -583,11 +599,28 @@ int sgmv_shrink(float* v, const void* x, const void* A_stack, const int32_t* seg
     hipStream_t st = (hipStream_t)stream;
     float* out = p.ksplit > 1 ? (float*)((char*)workspace + kCounterBytes) : v;
     const long long stride = (long long)num_rows * r;
-    with_dtype(dtype, [&](auto dt) {
-        using DT = decltype(dt);
-        dispatch_shrink<DT>(out, stride, x, A_stack, seg_indptr, adapter_ids, num_segments,
-                            num_rows, num_adapters, H1, r, p, st);
-    });
+    // Row-heavy calls: 16-row MFMA tiles over the same H1 ranges (each
+    // workgroup sums its range's LDS-sized chunks in order), so the
+    // workspace is the same as for the vector kernel.
+    const MfmaPlan mp = make_mfma_plan(num_rows, num_segments, H1, 8, r, dtype);
+    const long long mslots = mp.slots_a + mp.slots_b;
+    if (mslots > 0 && aligned16(x) && aligned16(A_stack) && use_mfma(num_rows, num_segments) &&
+        mslots * p.ksplit <= kMaxGrid) {
+        with_mfma_rank(dtype, r, [&](auto dt, auto rank) {
+            using DT = decltype(dt);
+            using T = typename DT::storage;
+            constexpr int R = decltype(rank)::value;
+            launch(&shrink_mfma_kernel<DT, R>, dim3((unsigned)(mslots * p.ksplit)), dim3(256), st,
+                   (const T*)x, (const T*)A_stack, seg_indptr, adapter_ids, num_segments,
+                   num_rows, num_adapters, H1, out, p.ksplit, p.h_per_split, mp.compact);
+        });
+    } else {
+        with_dtype(dtype, [&](auto dt) {
+            using DT = decltype(dt);
+            dispatch_shrink<DT>(out, stride, x, A_stack, seg_indptr, adapter_ids, num_segments,
+                                num_rows, num_adapters, H1, r, p, st);
+        });
+    }
     if ((rc = launch_status()) != SGMV_OK) return rc;
     if (p.ksplit > 1) {
         const long long n = stride;
@@ -612,6 +645,21 @@ int sgmv_expand(void* y, const float* v, const void* B_stack, const int32_t* seg
     const Plan p = make_plan(num_rows, num_segments, 1, r, dtype);
     if (!grid_fits(p, H2)) return SGMV_ERR_UNSUPPORTED;
     hipStream_t st = (hipStream_t)stream;
+    // Row-heavy calls: 16-row MFMA tiles, v read as the single "partial".
+    const MfmaPlan mp = make_mfma_plan(num_rows, num_segments, 8, H2, r, dtype);
+    const long long mslots = mp.slots_a + mp.slots_b;
+    if (mslots > 0 && aligned16(y) && aligned16(B_stack) && use_mfma(num_rows, num_segments) &&
+        mslots * mp.csplit <= kMaxGrid) {
+        with_mfma_rank(dtype, r, [&](auto dt, auto rank) {
+            using DT = decltype(dt);
+            using T = typename DT::storage;
+            constexpr int R = decltype(rank)::value;
+            launch(&expand_mfma_kernel<DT, R>, dim3((unsigned)(mslots * mp.csplit)), dim3(256), st,
+                   (T*)y, (const T*)B_stack, seg_indptr, adapter_ids, num_segments, num_rows,
+                   num_adapters, H2, scale, v, 1, mp.csplit, mp.compact);
+        });
+        return launch_status();
+    }
     with_dtype(dtype, [&](auto dt) {
         using DT = decltype(dt);
         dispatch_expand<DT>(y, v, 0, 1, B_stack, seg_indptr, adapter_ids, num_segments, num_rows,
