@@ -354,17 +354,17 @@ int launch_status() {
 template <typename DT, int R>
 void launch_shrink_vec(float* out, long long out_stride, const void* x, const void* A,
                        const int32_t* seg, const int32_t* ids, int S, int rows, int nad, int H1,
-                       const Plan& p, hipStream_t st) {
+                       const Plan& p, hipStream_t st, float* v_final, int* counters) {
     using T = typename DT::storage;
     const unsigned grid = (unsigned)(tile_slots(S, rows, p.rows) * p.ksplit);
     if (p.rows == 1)
         launch(&shrink_vec_kernel<DT, R, kShrinkThreads, 1, kShrinkPG>, dim3(grid),
                dim3(kShrinkThreads), st, out, out_stride, (const T*)x, (const T*)A, seg, ids, S,
-               rows, nad, H1, p.ksplit, p.h_per_split);
+               rows, nad, H1, p.ksplit, p.h_per_split, v_final, counters, kCounterStride);
     else
         launch(&shrink_vec_kernel<DT, R, kShrinkThreads, kShrinkRows, kShrinkPG>, dim3(grid),
                dim3(kShrinkThreads), st, out, out_stride, (const T*)x, (const T*)A, seg, ids, S,
-               rows, nad, H1, p.ksplit, p.h_per_split);
+               rows, nad, H1, p.ksplit, p.h_per_split, v_final, counters, kCounterStride);
 }
 
 template <typename DT>
@@ -378,29 +378,36 @@ void launch_shrink_generic(float* out, long long out_stride, const void* x, cons
                        seg, ids, S, rows, nad, H1, r, p.ksplit, p.h_per_split);
 }
 
+// Returns true when the launched kernel also reduced the partials into
+// v_final (vectorised kernel, v_final and counters given).
 template <typename DT>
-void dispatch_shrink(float* out, long long out_stride, const void* x, const void* A,
+bool dispatch_shrink(float* out, long long out_stride, const void* x, const void* A,
                      const int32_t* seg, const int32_t* ids, int S, int rows, int nad, int H1,
-                     int r, const Plan& p, hipStream_t st) {
+                     int r, const Plan& p, hipStream_t st, float* v_final = nullptr,
+                     int* counters = nullptr) {
     const bool vec = vec_rank(std::is_same<DT, F32>::value ? SGMV_F32 : SGMV_F16, r) &&
                      aligned16(A);
+    auto go = [&](auto rank) {
+        constexpr int R = decltype(rank)::value;
+        launch_shrink_vec<DT, R>(out, out_stride, x, A, seg, ids, S, rows, nad, H1, p, st,
+                                 v_final, counters);
+        return v_final != nullptr;
+    };
     if (vec) {
         switch (r) {
             case 4:
-                if constexpr (DT::kVec == 4) {
-                    launch_shrink_vec<DT, 4>(out, out_stride, x, A, seg, ids, S, rows, nad, H1, p, st);
-                    return;
-                }
+                if constexpr (DT::kVec == 4) return go(std::integral_constant<int, 4>{});
                 break;
-            case 8: launch_shrink_vec<DT, 8>(out, out_stride, x, A, seg, ids, S, rows, nad, H1, p, st); return;
-            case 16: launch_shrink_vec<DT, 16>(out, out_stride, x, A, seg, ids, S, rows, nad, H1, p, st); return;
-            case 32: launch_shrink_vec<DT, 32>(out, out_stride, x, A, seg, ids, S, rows, nad, H1, p, st); return;
-            case 64: launch_shrink_vec<DT, 64>(out, out_stride, x, A, seg, ids, S, rows, nad, H1, p, st); return;
-            case 128: launch_shrink_vec<DT, 128>(out, out_stride, x, A, seg, ids, S, rows, nad, H1, p, st); return;
+            case 8: return go(std::integral_constant<int, 8>{});
+            case 16: return go(std::integral_constant<int, 16>{});
+            case 32: return go(std::integral_constant<int, 32>{});
+            case 64: return go(std::integral_constant<int, 64>{});
+            case 128: return go(std::integral_constant<int, 128>{});
             default: break;
         }
     }
     launch_shrink_generic<DT>(out, out_stride, x, A, seg, ids, S, rows, nad, H1, r, p, st);
+    return false;
 }
 
 // -- expand dispatch ---------------------------------------------------------
@@ -604,6 +611,7 @@ int sgmv_shrink(float* v, const void* x, const void* A_stack, const int32_t* seg
     // workspace is the same as for the vector kernel.
     const MfmaPlan mp = make_mfma_plan(num_rows, num_segments, H1, 8, r, dtype);
     const long long mslots = mp.slots_a + mp.slots_b;
+    bool reduced = false;
     if (mslots > 0 && aligned16(x) && aligned16(A_stack) && use_mfma(num_rows, num_segments) &&
         mslots * p.ksplit <= kMaxGrid) {
         with_mfma_rank(dtype, r, [&](auto dt, auto rank) {
@@ -615,14 +623,21 @@ int sgmv_shrink(float* v, const void* x, const void* A_stack, const int32_t* seg
                    num_rows, num_adapters, H1, out, p.ksplit, p.h_per_split, mp.compact);
         });
     } else {
+        // With a split, the tile's last workgroup reduces the partials into v
+        // (tile counters at the start of the workspace) when the tiles fit
+        // the counters; otherwise a reduction launch follows.
+        const bool in_kernel =
+            p.ksplit > 1 && tile_slots(num_segments, num_rows, p.rows) <= kCounterSlots;
         with_dtype(dtype, [&](auto dt) {
             using DT = decltype(dt);
-            dispatch_shrink<DT>(out, stride, x, A_stack, seg_indptr, adapter_ids, num_segments,
-                                num_rows, num_adapters, H1, r, p, st);
+            reduced = dispatch_shrink<DT>(out, stride, x, A_stack, seg_indptr, adapter_ids,
+                                          num_segments, num_rows, num_adapters, H1, r, p, st,
+                                          in_kernel ? v : nullptr,
+                                          in_kernel ? (int*)workspace : nullptr);
         });
     }
     if ((rc = launch_status()) != SGMV_OK) return rc;
-    if (p.ksplit > 1) {
+    if (p.ksplit > 1 && !reduced) {
         const long long n = stride;
         const unsigned grid = (unsigned)((n + 255) / 256);
         launch(&reduce_partials_kernel, dim3(grid), dim3(256), st, v, out, stride,

@@ -95,14 +95,17 @@ struct ReduceScatter {
 // x is read as scalars (it is L1/L2-resident: all lanes of the workgroup
 // touch the same RB rows).
 //
-// out[p * out_stride + row * R + k] receives the chunk-p partial sums.
+// out[p * out_stride + row * R + k] receives the chunk-p partial sums.  With
+// v_final (and zeroed tile counters), the tile's last workgroup also sums
+// them into v_final[row * R + k], which spares a separate reduction launch.
 // ---------------------------------------------------------------------------
 template <typename DT, int R, int NT, int RB, int PG>
 __global__ __launch_bounds__(NT) void shrink_vec_kernel(
     float* __restrict__ out, long long out_stride, const typename DT::storage* __restrict__ x,
     const typename DT::storage* __restrict__ A_stack, const int* __restrict__ seg_indptr,
     const int* __restrict__ adapter_ids, int S, int num_rows, int num_adapters, int H1,
-    int ksplit, int h_per_split) {
+    int ksplit, int h_per_split, float* __restrict__ v_final = nullptr,
+    int* __restrict__ counters = nullptr, int counter_stride = 0) {
     using st = typename DT::storage;
     constexpr int VEC = DT::kVec;
     static_assert(R % VEC == 0, "rank must be a multiple of the vector width");
@@ -189,7 +192,50 @@ __global__ __launch_bounds__(NT) void shrink_vec_kernel(
         float sum = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) sum += s_red[w][t];
-        if (i < nrows) out[(long long)p * out_stride + (long long)(tile.row0 + i) * R + k] = sum;
+        if (i < nrows) {
+            float* dst = &out[(long long)p * out_stride + (long long)(tile.row0 + i) * R + k];
+            if (v_final) __hip_atomic_store(dst, sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else *dst = sum;
+        }
+    }
+    if (!v_final) return;
+
+    // In-kernel reduction: the last of the tile's ksplit workgroups to
+    // arrive (told by its counter addition, so no workgroup waits) sums the
+    // chunks' partials in chunk order, as reduce_partials_kernel would, and
+    // writes v.  Partials are stored and read at agent scope (write-through,
+    // no L2 write-back), each wave's stores acknowledged before the count;
+    // the last arriver returns the counter to zero.
+    __shared__ int s_last;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+        int* cnt = &counters[(long long)g * counter_stride];
+        const int before = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = before == ksplit - 1;
+        if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = last;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    for (int t = tid; t < nrows * R; t += NT) {
+        const int i = t / R;
+        const int k = t - i * R;
+        float* src = &out[(long long)(tile.row0 + i) * R + k];
+        float sum = 0.f;
+        for (int c0 = 0; c0 < ksplit; c0 += 8) {
+            float pv[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                pv[u] = c0 + u < ksplit ? __hip_atomic_load(src + (long long)(c0 + u) * out_stride,
+                                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                        : 0.f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (c0 + u < ksplit) sum += pv[u];
+        }
+        v_final[(long long)(tile.row0 + i) * R + k] = sum;
     }
 }
 

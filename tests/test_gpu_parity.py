@@ -286,8 +286,10 @@ def test_workspace_reused_across_shapes():
     shapes = [(0, "f16", 4096, 4096, 16, 64, 64, 64), (1, "bf16", 1024, 3072, 64, 9, 200, 40),
               (2, "f16", 2048, 1024, 8, 5, 30, 3), (3, "f32", 512, 768, 16, 7, 300, 90)]
     work = [wl.small_random(sd, dt, H1, H2, r, N, R, S) for sd, dt, H1, H2, r, N, R, S in shapes]
-    need = max(sg.lora_apply_workspace_bytes(w.num_rows, w.num_segments, w.H1, w.H2, w.r,
-                                             torch_dtype(w.dtype)) for w in work)
+    need = max(max(sg.lora_apply_workspace_bytes(w.num_rows, w.num_segments, w.H1, w.H2, w.r,
+                                                 torch_dtype(w.dtype)),
+                   sg.shrink_workspace_bytes(w.num_rows, w.num_segments, w.H1, w.r,
+                                             torch_dtype(w.dtype))) for w in work)
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
     for w in work + work[::-1] + work:
         d = to_device(w)
@@ -297,6 +299,48 @@ def test_workspace_reused_across_shapes():
         y_ref, _ = oracle.lora_apply(w.y0, w.x, w.A, w.B, w.seg_indptr, w.adapter_ids, w.scale)
         assert_close(y.double().cpu().numpy(), y_ref, w.dtype, w.name)
         assert int(ws[:262144].view(torch.int32).abs().sum()) == 0
+        # sgmv_shrink on the same workspace (its tile counters sit there too)
+        v = torch.zeros(w.num_rows, w.r, dtype=torch.float32, device="cuda")
+        sg.sgmv_shrink(v, d["x"], d["A"], d["seg"], d["ids"], workspace=ws)
+        torch.cuda.synchronize()
+        v_ref = oracle.shrink(w.x, w.A, w.seg_indptr, w.adapter_ids)
+        covered = np.zeros(w.num_rows, bool)
+        for k in range(w.num_segments):
+            covered[w.seg_indptr[k]:w.seg_indptr[k + 1]] = True
+        assert_close(v.double().cpu().numpy()[covered], v_ref[covered], w.dtype, w.name + " shrink")
+        assert int(ws[:262144].view(torch.int32).abs().sum()) == 0
+
+
+def test_shrink_in_kernel_reduction_is_deterministic():
+    """Decode-shaped sgmv_shrink splits H1 over several workgroups per row
+    and the last of them sums the chunks in order: repeated calls give the
+    same bits, rows outside every segment keep their contents, and the tile
+    counters are left at zero."""
+    import torch
+    import segmented_gather_gemv_sgmv_amd as sg
+    w = wl.small_random(11, "f16", 4096, 1024, 16, 40, 48, 40, uncovered_tail=8)
+    d = to_device(w)
+    need = sg.shrink_workspace_bytes(w.num_rows, w.num_segments, w.H1, w.r, torch.float16)
+    assert need > 262144, "the shape must split H1 (partials after the counters)"
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(3):
+        v = torch.full((w.num_rows, w.r), 7.0, dtype=torch.float32, device="cuda")
+        sg.sgmv_shrink(v, d["x"], d["A"], d["seg"], d["ids"], workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:262144].view(torch.int32).abs().sum()) == 0
+        outs.append(v.clone())
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
+    got = outs[0].double().cpu().numpy()
+    v_ref = oracle.shrink(w.x, w.A, w.seg_indptr, w.adapter_ids)
+    R = w.num_rows
+    end = int(w.seg_indptr[-1])
+    assert end <= R - 8
+    assert np.all(got[end:] == 7.0)
+    covered = np.zeros(R, bool)
+    for k in range(w.num_segments):
+        covered[w.seg_indptr[k]:w.seg_indptr[k + 1]] = True
+    assert_close(got[covered], v_ref[covered], w.dtype, "decode shrink")
 
 
 @pytest.mark.parametrize("seed,dtype,H1,H2,r,N,R,S,tail", [
