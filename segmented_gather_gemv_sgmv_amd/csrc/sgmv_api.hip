@@ -625,7 +625,9 @@ int sgmv_shrink(float* v, const void* x, const void* A_stack, const int32_t* seg
     } else {
         // With a split, the tile's last workgroup reduces the partials into v
         // (tile counters at the start of the workspace) when the tiles fit
-        // the counters; otherwise a reduction launch follows.
+        // the counters; otherwise (or after the general kernel) a reduction
+        // launch follows.  The plan splits only below 512 tile slots, so for
+        // the vectorised kernel the tiles always fit.
         const bool in_kernel =
             p.ksplit > 1 && tile_slots(num_segments, num_rows, p.rows) <= kCounterSlots;
         with_dtype(dtype, [&](auto dt) {

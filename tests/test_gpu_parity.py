@@ -383,5 +383,14 @@ def test_tile_mappings(S, R, lengths_kind):
     w = wl.make_workload("decode_map", "f16", 1024, 1536, 16, 24, lengths, ids, 0.75,
                          seed=S, num_rows=R)
     assert w.seg_indptr[-1] <= R
-    y_ref, _ = oracle.lora_apply(w.y0, w.x, w.A, w.B, w.seg_indptr, w.adapter_ids, w.scale)
+    y_ref, v_ref = oracle.lora_apply(w.y0, w.x, w.A, w.B, w.seg_indptr, w.adapter_ids, w.scale)
     assert_close(gpu_lora_apply(w), y_ref, "f16", f"decode mapping {lengths_kind}")
+    # sgmv_shrink over the same table: thousands of one-row tiles take no
+    # H1 split ("ones", "sparse"); the mixed case splits H1 and the tiles'
+    # last workgroups reduce it in-kernel.
+    cov = np.zeros(R, bool)
+    for k in range(S):
+        cov[w.seg_indptr[k]:w.seg_indptr[k + 1]] = True
+    v = gpu_shrink(w, fill=-2.0)
+    assert_close(v[cov], v_ref[cov], "f16", f"decode mapping shrink {lengths_kind}")
+    assert np.all(v[~cov] == -2.0)
