@@ -106,6 +106,24 @@ def test_integer_inputs_match_bit_for_bit(dtype, r):
     assert np.array_equal(gpu_lora_apply(w, d), y_ref)
     cov = int(w.seg_indptr[-1])
     assert np.array_equal(gpu_shrink(w, d)[:cov], v_ref[:cov])
+    y_e = oracle.expand(w.y0, v_ref.astype(np.float32), w.B, w.seg_indptr, w.adapter_ids, w.scale)
+    assert np.array_equal(gpu_expand(w, v_ref, d), y_e)
+
+
+@pytest.mark.parametrize("dtype,r,H1,R,S", [("f16", 16, 2048, 600, 3), ("bf16", 64, 1024, 520, 4),
+                                            ("f16", 128, 2048, 2400, 4)])
+def test_integer_inputs_row_heavy_bit_for_bit(dtype, r, H1, R, S):
+    """Row-heavy integer cases: every entry point runs on the MFMA tiles (the
+    last one splits H1 into grouped chunk ranges) and must match exactly."""
+    w = wl.integer_exact(7 * r + R, dtype, H1, 1024, r, 5, R, S, density=0.05, scale=2.0)
+    y_ref, v_ref = oracle.lora_apply(w.y0, w.x, w.A, w.B, w.seg_indptr, w.adapter_ids, w.scale)
+    assert np.abs(y_ref).max() < 256 and np.abs(v_ref).max() < 2048
+    d = to_device(w)
+    assert np.array_equal(gpu_lora_apply(w, d), y_ref)
+    cov = int(w.seg_indptr[-1])
+    assert np.array_equal(gpu_shrink(w, d)[:cov], v_ref[:cov])
+    y_e = oracle.expand(w.y0, v_ref.astype(np.float32), w.B, w.seg_indptr, w.adapter_ids, w.scale)
+    assert np.array_equal(gpu_expand(w, v_ref, d), y_e)
 
 
 def test_long_segments_and_many_segments():
