@@ -614,14 +614,19 @@ int sgmv_shrink(float* v, const void* x, const void* A_stack, const int32_t* seg
     bool reduced = false;
     if (mslots > 0 && aligned16(x) && aligned16(A_stack) && use_mfma(num_rows, num_segments) &&
         mslots * p.ksplit <= kMaxGrid) {
+        // A split is reduced in-kernel when the tiles fit the counters.
+        const bool in_kernel = p.ksplit > 1 && mslots <= kCounterSlots;
         with_mfma_rank(dtype, r, [&](auto dt, auto rank) {
             using DT = decltype(dt);
             using T = typename DT::storage;
             constexpr int R = decltype(rank)::value;
             launch(&shrink_mfma_kernel<DT, R>, dim3((unsigned)(mslots * p.ksplit)), dim3(256), st,
                    (const T*)x, (const T*)A_stack, seg_indptr, adapter_ids, num_segments,
-                   num_rows, num_adapters, H1, out, p.ksplit, p.h_per_split, mp.compact);
+                   num_rows, num_adapters, H1, out, p.ksplit, p.h_per_split, mp.compact,
+                   in_kernel ? v : nullptr, in_kernel ? (int*)workspace : nullptr,
+                   kCounterStride);
         });
+        reduced = in_kernel;
     } else {
         // With a split, the tile's last workgroup reduces the partials into v
         // (tile counters at the start of the workspace) when the tiles fit
@@ -718,7 +723,8 @@ int lora_apply(void* y, const void* x, const void* A_stack, const void* B_stack,
             if (sp.ok) {
                 launch(&shrink_mfma_kernel<DT, R>, dim3((unsigned)sp.grid_shrink), dim3(256), st,
                        (const T*)x, (const T*)A_stack, seg_indptr, adapter_ids, num_segments,
-                       num_rows, num_adapters, H1, part, sp.ksplit, sp.h_per_split, sp.compact);
+                       num_rows, num_adapters, H1, part, sp.ksplit, sp.h_per_split, sp.compact,
+                       (float*)nullptr, (int*)nullptr, 0);
                 if (t_pending != hipSuccess) return;  // no expand over partials never written
                 launch(&expand_mfma_kernel<DT, R>, dim3((unsigned)sp.grid_expand), dim3(256), st,
                        (T*)y, (const T*)B_stack, seg_indptr, adapter_ids, num_segments, num_rows,

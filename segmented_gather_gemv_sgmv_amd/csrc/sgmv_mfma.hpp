@@ -475,7 +475,8 @@ __global__ __launch_bounds__(256) void shrink_mfma_kernel(
     const typename DT::storage* __restrict__ x, const typename DT::storage* __restrict__ A_stack,
     const int* __restrict__ seg_indptr, const int* __restrict__ adapter_ids, int S, int num_rows,
     int num_adapters, int H1, float* __restrict__ partials, int ksplit, int h_per_split,
-    int compact) {
+    int compact, float* __restrict__ v_final = nullptr, int* __restrict__ counters = nullptr,
+    int counter_stride = 0) {
     using Sh = MfmaShape<R>;
     constexpr int T = Sh::kT;
     constexpr int NT = Sh::kNT;
@@ -483,6 +484,7 @@ __global__ __launch_bounds__(256) void shrink_mfma_kernel(
     __shared__ int s_scan[tile_scan_ints<NT>()];
     __shared__ __align__(16) uint16_t s_a[Sh::kKcMax * R];
     __shared__ float s_red[NW * 16 * R];
+    __shared__ int s_last;
 
     const int g = (int)(blockIdx.x / (unsigned)ksplit);
     const int p = (int)(blockIdx.x % (unsigned)ksplit);
@@ -501,12 +503,55 @@ __global__ __launch_bounds__(256) void shrink_mfma_kernel(
     float* out = partials + (long long)p * num_rows * R + (long long)tile.row0 * R;
     for (int c_lo = h_lo; c_lo < h_hi; c_lo += Sh::kKcMax) {
         const bool first = c_lo == h_lo;
+        const bool final_chunk = c_lo + Sh::kKcMax >= h_hi;
         shrink_chunk_mfma<DT, R>(A_stack + (long long)tile.adapter * H1 * R,
                                  x + (long long)tile.row0 * H1, tile.nrows, H1, c_lo,
                                  min(h_hi, c_lo + Sh::kKcMax), s_a, s_red,
                                  [&](int i, int k, float v) {
-                                     out[i * R + k] = first ? v : out[i * R + k] + v;
+                                     const float val = first ? v : out[i * R + k] + v;
+                                     if (v_final && final_chunk)
+                                         __hip_atomic_store(&out[i * R + k], val, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT);
+                                     else
+                                         out[i * R + k] = val;
                                  });
+    }
+    if (!v_final) return;
+
+    // In-kernel reduction (sgmv_shrink): the last of the tile's ksplit
+    // workgroups to arrive sums the ranges' partials in order into v_final,
+    // as in shrink_vec_kernel; the partials' final stores are write-through
+    // and acknowledged before the count, and the counter returns to zero.
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int* cnt = &counters[(long long)g * counter_stride];
+        const int before = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = before == ksplit - 1;
+        if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = last;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    const long long stride = (long long)num_rows * R;
+    for (int t = threadIdx.x; t < tile.nrows * R; t += NT) {
+        const int i = t / R;
+        const int k = t - i * R;
+        float* src = partials + (long long)(tile.row0 + i) * R + k;
+        float sum = 0.f;
+        for (int c0 = 0; c0 < ksplit; c0 += 8) {
+            float pv[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                pv[u] = c0 + u < ksplit ? __hip_atomic_load(src + (c0 + u) * stride,
+                                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                        : 0.f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (c0 + u < ksplit) sum += pv[u];
+        }
+        v_final[(long long)(tile.row0 + i) * R + k] = sum;
     }
 }
 
