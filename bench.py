@@ -165,8 +165,28 @@ class BenchState:
         return g
 
 
+# Byte offset of the sticky flag in the workspace: the last int of the
+# 256 KiB counter region (include/sgmv.h, "Workspace").
+FLAG_OFFSET = 65536 * 4 - 4
+
+
+def read_flag(ws) -> int:
+    import torch
+    return int(ws[FLAG_OFFSET:FLAG_OFFSET + 4].view(torch.int32).item())
+
+
+def clear_flag(ws) -> None:
+    ws[FLAG_OFFSET:FLAG_OFFSET + 4].zero_()
+
+
 def run_gpu(w, steps: int, warmup: int, device="cuda:0", row_ids=None, projections=1,
-            warm=False, entry="apply"):
+            warm=False, entry="apply", replays=5):
+    """Times `steps` consecutive steps captured in one HIP graph, replayed
+    `replays` times, each replay bracketed by HIP events on the replay
+    stream; the per-step time is the median over the replays, so that it
+    does not move with the graph length.  Also reads the fused kernels'
+    sticky flag (an expand workgroup stopped waiting for its shrink
+    workgroups and recomputed its input) over the timed replays."""
     import torch
     per_set = (w.x.size + w.A.size + w.B.size + w.y0.size) * w.elem_bytes * projections
     nsets = 1 if warm else max(1, min(512, math.ceil(ROTATE_BYTES / max(per_set, 1))))
@@ -176,16 +196,22 @@ def run_gpu(w, steps: int, warmup: int, device="cuda:0", row_ids=None, projectio
     torch.cuda.synchronize(device)
     graph = st.capture(steps, first=warmup)
     torch.cuda.synchronize(device)
-    stream = torch.cuda.current_stream(device)
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    start.record(stream)
-    graph.replay()
-    end.record(stream)
+    clear_flag(st.workspace)
     torch.cuda.synchronize(device)
+    stream = torch.cuda.current_stream(device)
+    t0 = time.perf_counter()
+    per_replay_ms = []
+    for _ in range(max(1, replays)):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        graph.replay()
+        end.record(stream)
+        torch.cuda.synchronize(device)
+        per_replay_ms.append(start.elapsed_time(end))
     wall = time.perf_counter() - t0
-    gpu_ms = start.elapsed_time(end)
+    flag = read_flag(st.workspace)
+    gpu_ms = float(np.median(per_replay_ms))
     # Spread: a graph of `chunk` steps (every buffer set at least once)
     # replayed `reps` times, each replay timed on its own; the per-call means
     # of the replays give p10 / p50 / p90.
@@ -204,7 +230,10 @@ def run_gpu(w, steps: int, warmup: int, device="cuda:0", row_ids=None, projectio
         samples.append(a.elapsed_time(b) * 1e3 / chunk)
     pct = np.percentile(np.asarray(samples), [10, 50, 90]).tolist()
     return dict(gpu_ms=gpu_ms, wall_s=wall, nsets=nsets, per_set_bytes=per_set,
-                us_p10_p50_p90=pct, spread_steps=chunk, spread_replays=reps)
+                us_p10_p50_p90=pct, spread_steps=chunk, spread_replays=reps,
+                replays=len(per_replay_ms),
+                us_per_step_each_replay=[m * 1e3 / steps for m in per_replay_ms],
+                fallback_flag=flag)
 
 
 KERNEL_SOURCES = ("segmented_gather_gemv_sgmv_amd/csrc/sgmv_api.hip",
@@ -360,22 +389,83 @@ def copy_calibration(nbytes: int, reps: int = 20):
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
+def _host_threads() -> int:
+    """Threads the host offers this process: its CPU affinity, capped by
+    OMP_NUM_THREADS when that is set."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp and omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, n)
+
+
+def _row_groups(w, groups: int):
+    """The batch cut into `groups` contiguous row ranges of about equal size,
+    each with the segment table clipped to its rows (a segment split at a
+    cut becomes two segments with the same adapter: the rows are
+    independent).  Each range is an independent sub-batch for one thread."""
+    R = w.num_rows
+    bounds = [round(R * g / groups) for g in range(groups + 1)]
+    out = []
+    for lo, hi in zip(bounds[:-1], bounds[1:]):
+        if hi <= lo:
+            continue
+        s_lo = w.seg_indptr[:-1]
+        s_hi = w.seg_indptr[1:]
+        keep = (s_hi > lo) & (s_lo < hi)
+        a = np.clip(s_lo[keep], lo, hi) - lo
+        b = np.clip(s_hi[keep], lo, hi) - lo
+        seg = np.concatenate([a[:1], b]).astype(np.int32) if keep.any() else np.zeros(1, np.int32)
+        out.append((lo, hi, seg, w.adapter_ids[keep].astype(np.int32)))
+    return out
+
+
 def cpu_baseline(w, budget_s: float = 10.0):
-    """The CPU oracle (single thread, plain fp64 loops) on the same batch."""
+    """The CPU oracle (plain fp64 loops, as it stands) on the same batch: one
+    thread on the whole batch, then every host thread at once, each running
+    the oracle on its own contiguous range of rows (the oracle's ctypes
+    call releases the GIL, so the threads run in parallel).  Each leg runs
+    for about ``budget_s`` / 2 seconds."""
     import oracle
+    from concurrent.futures import ThreadPoolExecutor
     orc = oracle.get()
+    rows_per_batch = int(w.seg_lengths.sum())
+
     calls = 0
     t0 = time.perf_counter()
     while True:
         orc.lora_apply(w.y0, w.x, w.A, w.B, w.seg_indptr, w.adapter_ids, w.scale)
         calls += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
+        el1 = time.perf_counter() - t0
+        if el1 >= budget_s / 2:
             break
-    rows = int(w.seg_lengths.sum()) * calls
-    return dict(value=rows / el, unit="rows/s", cores=1, kind="oracle",
-                sample=f"{calls} full {w.num_rows}-row batches of the same workload "
-                       f"({el:.1f} s, one thread)")
+    single = rows_per_batch * calls / el1
+
+    nthreads = _host_threads()
+    groups = _row_groups(w, nthreads)
+
+    def one(g):
+        lo, hi, seg, ids = g
+        orc.lora_apply(w.y0[lo:hi], w.x[lo:hi], w.A, w.B, seg, ids, w.scale)
+
+    batches = 0
+    with ThreadPoolExecutor(max_workers=len(groups)) as pool:
+        t0 = time.perf_counter()
+        while True:
+            list(pool.map(one, groups))
+            batches += 1
+            el2 = time.perf_counter() - t0
+            if el2 >= budget_s / 2:
+                break
+    multi = rows_per_batch * batches / el2
+    return dict(value=multi, unit="rows/s", cores=len(groups), kind="oracle",
+                sample=f"{batches} full {w.num_rows}-row batches of the same workload over "
+                       f"{len(groups)} threads, each thread a contiguous range of rows "
+                       f"({el2:.1f} s); single thread: {calls} batches ({el1:.1f} s)",
+                single_thread={"value": single, "unit": "rows/s", "cores": 1},
+                nproc=os.cpu_count(), affinity=(len(os.sched_getaffinity(0))
+                                                if hasattr(os, "sched_getaffinity") else None),
+                OMP_NUM_THREADS=os.environ.get("OMP_NUM_THREADS"))
 
 
 def adapter_load(w, reps: int = 20, device="cuda:0"):
@@ -439,6 +529,7 @@ WORKLOADS = {
     "prefill": lambda wl: wl.prefill(seed=0),
     "mlp_up_decode": lambda wl: wl.mlp_up_decode(seed=0),
     "tiny": lambda wl: wl.tiny(seed=0),
+    "mixed": lambda wl: wl.mixed_batch(seed=0),
 }
 WORKLOAD_SHAPES = {
     "llama7b_decode": "Llama-2-7B decode shapes",
@@ -447,6 +538,7 @@ WORKLOAD_SHAPES = {
     "prefill": "Llama-2-7B prefill shapes",
     "mlp_up_decode": "Llama-13B up-projection decode shapes",
     "tiny": "tiny shapes",
+    "mixed": "Llama-2-7B shapes, two 512-row prefill segments and 128 one-row decode segments",
 }
 
 
@@ -552,6 +644,10 @@ def main(argv=None):
                             "expand": "sgmv_expand"}[entry],
         },
         "us_per_call": step_s * 1e6,
+        "timing": f"median over {res['replays']} replays of the {args.steps}-step graph, "
+                  "HIP events on the replay stream",
+        "us_per_call_each_replay": res["us_per_step_each_replay"],
+        "fallback_flag": res["fallback_flag"],
         "us_per_call_p10_p50_p90": res["us_p10_p50_p90"],
         "spread": f"per-call means of {res['spread_replays']} separately timed replays "
                   f"of a {res['spread_steps']}-step graph",

@@ -158,14 +158,23 @@ class _WorkspaceCache:
 
     Calls on one stream run in order, so they can share its buffer; the
     library leaves the buffer's counter region zero after every call, as it
-    requires on entry."""
+    requires on entry.  Not used while a stream is capturing a graph: a
+    captured call would keep the buffer's address in the graph, and the
+    cache may later replace that buffer or hand it to eager calls on a
+    stream the graph does not order against.  Graph captures must pass an
+    explicit workspace (see ``need_workspace``)."""
 
     def __init__(self):
         self._bufs = {}
         self._lock = threading.Lock()
 
-    def get(self, device, stream: int, nbytes: int):
+    def get(self, device, stream: int, nbytes: int, what: str):
         torch = _torch()
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError(
+                f"{what}: no workspace given while a HIP graph is being captured; pass "
+                f"workspace= a zeroed uint8 device tensor of at least {nbytes} bytes, owned by "
+                "the caller for as long as the graph may be replayed")
         key = (device, stream)
         with self._lock:
             buf = self._bufs.get(key)
@@ -204,7 +213,7 @@ def sgmv_shrink(v, x, A_stack, seg_indptr, adapter_ids, workspace=None):
     stream = _stream_ptr(dev)
     need = shrink_workspace_bytes(R, S, H1, r, x.dtype)
     if workspace is None and need > 0:
-        workspace = _workspaces.get(dev, stream, need)
+        workspace = _workspaces.get(dev, stream, need, "sgmv_shrink")
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().sgmv_shrink(v.data_ptr(), x.data_ptr(), A_stack.data_ptr(), seg_indptr.data_ptr(),
@@ -255,7 +264,7 @@ def lora_apply(y, x, A_stack, B_stack, seg_indptr, adapter_ids, scale=1.0, works
     stream = _stream_ptr(dev)
     need = lora_apply_workspace_bytes(R, S, H1, H2, r, x.dtype)
     if workspace is None:
-        workspace = _workspaces.get(dev, stream, need)
+        workspace = _workspaces.get(dev, stream, need, "lora_apply")
     _check(lib().lora_apply(y.data_ptr(), x.data_ptr(), A_stack.data_ptr(), B_stack.data_ptr(),
                             seg_indptr.data_ptr(), adapter_ids.data_ptr(), S, R, N, H1, H2, r,
                             float(scale), dt, workspace.data_ptr(),
@@ -303,7 +312,7 @@ def lora_linear(x, W, A_stack, B_stack, seg_indptr, adapter_ids, scale=1.0, bias
     stream = _stream_ptr(dev)
     need = lora_linear_workspace_bytes(R, S, H1, H2, r, x.dtype)
     if workspace is None:
-        workspace = _workspaces.get(dev, stream, need)
+        workspace = _workspaces.get(dev, stream, need, "lora_linear")
     _check(lib().lora_linear(out.data_ptr(), x.data_ptr(), W.data_ptr(),
                              None if bias is None else bias.data_ptr(), A_stack.data_ptr(),
                              B_stack.data_ptr(), seg_indptr.data_ptr(), adapter_ids.data_ptr(),
@@ -357,7 +366,7 @@ def lora_apply_multi(problems, seg_indptr, adapter_ids, workspace=None):
     if need == 0:
         raise SGMVError(4, "lora_apply_multi_workspace_bytes")
     if workspace is None:
-        workspace = _workspaces.get(dev, stream, need)
+        workspace = _workspaces.get(dev, stream, need, "lora_apply_multi")
     _check(lib().lora_apply_multi(parr, len(problems), seg_indptr.data_ptr(),
                                   adapter_ids.data_ptr(), S, R, N, r, dt, workspace.data_ptr(),
                                   workspace.numel() * workspace.element_size(), stream),

@@ -10,11 +10,14 @@
 // section 2.2).
 //
 // Items.  Workgroup b < slots*ksplit is shrink item (tile g, H1 chunk p): it
-// writes the chunk's partial sums of v for the tile rows, then adds one to
-// the tile's arrival counter (release, agent scope).  Workgroup b beyond is
-// expand item (tile g, column chunk c): it issues its B and y loads, waits
-// until the tile's counter reaches ksplit (acquire, agent scope), sums the
-// partials in chunk order and updates y.
+// writes the chunk's partial sums of v for the tile rows, waits until those
+// stores are acknowledged, then adds one to the tile's arrival counter.
+// Workgroup b beyond is expand item (tile g, column chunk c): it issues its
+// B and y loads, polls until the tile's counter reaches ksplit, sums the
+// partials in chunk order and updates y.  Every access to the partials and
+// the counter is a relaxed atomic at agent scope; the ordering comes from
+// waiting on the memory counters, not from release/acquire (see "Hand-off
+// without L2 write-backs" below).
 //
 // Progress.  Shrink items never wait, and a workgroup's index is below every
 // expand index, so on hardware that dispatches each XCD's workgroups in index
@@ -24,15 +27,21 @@
 // either way and the kernel never hangs.
 //
 // Hand-off without L2 write-backs.  A release fence at agent scope writes
-// back the whole L2 of the XCD and costs microseconds per workgroup, so the
-// partials never sit in L2 as plain data: they are written with agent-scope
-// atomic stores (write-through to the device coherence point), every wave
-// waits until its stores are acknowledged (s_waitcnt vmcnt(0)) before the
-// workgroup barrier, and only then does thread 0 bump the arrival counter.
-// Readers poll the counter and read the partials with agent-scope atomic
-// loads, which are served from the coherence point and never from a stale
-// cache line.  Every access to shared data is thus coherent at agent scope,
-// and the counter is published only after the data it announces.
+// back the whole L2 of the XCD (measured at microseconds per workgroup) and
+// an acquire invalidates it, so the protocol uses neither.  The partials
+// are written with relaxed agent-scope atomic stores, which gfx950 performs
+// write-through to the device coherence point; every wave waits until its
+// stores are acknowledged (s_waitcnt vmcnt(0)) before the workgroup
+// barrier, and only then does thread 0 add to the arrival counter.  Readers
+// poll the counter and read the partials with relaxed agent-scope atomic
+// loads, which bypass the non-coherent caches.  The counter is thus
+// published only after the data it announces has reached the coherence
+// point, and no reader can see a stale copy.  This rests on how gfx950
+// implements agent-scope atomics (write-through stores, cache-bypassing
+// loads) and on the store acknowledgement, not on the HIP memory model's
+// release/acquire rules, which would demand the fences above; the tests
+// exercise it (bit-identity with the self-contained path, determinism,
+// graph replays).
 //
 // Counters.  counters[g * counter_stride] of tile slot g (one cache line per
 // tile, so that atomics of different tiles do not contend) counts the
@@ -304,8 +313,8 @@ __device__ __forceinline__ void fused_item(
                             : make_uint4(0, 0, 0, 0);
 
             if (tid == 0) {
-                // Poll with relaxed loads (no cache invalidation per poll);
-                // one acquire fence once the count is complete.
+                // Poll with relaxed agent-scope loads (no cache invalidation
+                // per poll); the partials are then read the same way.
                 const int ok = wait_for_producers(&counters[g * counter_stride], ksplit, wait_ticks);
                 s_flag = ok;
             }

@@ -344,7 +344,7 @@ __global__ __launch_bounds__(kLinThreads) void linear_lora_kernel(
     // The segment table (when it fits LDS) is loaded up front, beside the
     // first chunks: the epilogue then finds each row's adapter in LDS rather
     // than by a chain of dependent global loads.
-    const bool seg_lds = S <= kLinSegLds;
+    const bool seg_lds = S > 0 && S <= kLinSegLds;  // no table is read when S == 0
     constexpr int kSegU = (kLinSegLds + 1 + kLinThreads - 1) / kLinThreads;
     int seg_r[kSegU], ids_r[kSegU];
 #pragma unroll

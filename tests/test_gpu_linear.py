@@ -48,10 +48,14 @@ def _gpu_linear(w, W, b, d=None, seg=None, ids=None):
     return y.double().cpu().numpy()
 
 
-def _oracle(w, W, b, seg=None, ids=None):
+def _oracle(w, W, b, seg=None, ids=None, absolute=False):
+    """The oracle's adapted layer; with ``absolute``, on the inputs' absolute
+    values (the magnitude of each element's terms, for the float32 bound)."""
     seg = w.seg_indptr if seg is None else seg
     ids = w.adapter_ids if ids is None else ids
-    return oracle.lora_linear(w.x, W, b, w.A, w.B, seg, ids, w.scale)
+    f = np.abs if absolute else (lambda a: a)
+    return oracle.lora_linear(f(w.x), f(W), None if b is None else f(b), f(w.A), f(w.B), seg,
+                              ids, f(w.scale))
 
 
 # (seed, dtype, H1, H2, r, N, R, S, uncovered tail, bias)
@@ -74,7 +78,8 @@ def test_random_shapes(case):
     w = wl.small_random(seed, dtype, H1, H2, r, N, R, S, uncovered_tail=tail)
     W, b = wl.base_layer(seed, dtype, H1, H2, bias=bias)
     print(f"lora_linear {case}", flush=True)
-    assert_close(_gpu_linear(w, W, b), _oracle(w, W, b), dtype, str(case))
+    assert_close(_gpu_linear(w, W, b), _oracle(w, W, b), dtype, str(case),
+                 _oracle(w, W, b, absolute=True))
 
 
 @pytest.mark.parametrize("dtype,R,H1,H2,r", [("f16", 64, 256, 128, 16), ("bf16", 150, 192, 264, 8),
@@ -99,6 +104,33 @@ def test_without_segments_is_the_base_layer():
     got = _gpu_linear(w, W, b, d, empty_seg, empty_ids)
     ref = _oracle(w, W, b, np.zeros(1, np.int32), np.zeros(0, np.int32))
     assert_close(got, ref, "f16", "no segments")
+
+
+@pytest.mark.parametrize("rows", [40, 150], ids=["skinny_tiles", "square_tiles"])
+def test_c_abi_no_segments_null_tables(rows):
+    """num_segments == 0 with NULL seg_indptr, adapter_ids and stacks, as the
+    header allows, through the matrix-core tiles (fp16, sizes multiples of 8,
+    aligned pointers): the kernel must read no table and return the base
+    layer."""
+    import torch
+    import segmented_gather_gemv_sgmv_amd as sg
+    H1, H2 = 256, 192
+    w = wl.small_random(21, "f16", H1, H2, 16, 2, rows, 2)
+    W, b = wl.base_layer(21, "f16", H1, H2)
+    x = _dev(w.x, "f16")
+    Wd = _dev(W, "f16")
+    bd = _dev(b, "f16")
+    y = torch.full((rows, H2), 7.0, dtype=torch.float16, device="cuda:0")
+    lib = sg.lib()
+    need = int(lib.lora_linear_workspace_bytes(rows, 0, H1, H2, 16, sg.SGMV_F16))
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda:0")
+    rc = lib.lora_linear(y.data_ptr(), x.data_ptr(), Wd.data_ptr(), bd.data_ptr(), None, None,
+                         None, None, 0, rows, 0, H1, H2, 16, 2.0, sg.SGMV_F16, ws.data_ptr(),
+                         ws.numel(), torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, sg.STATUS.get(rc, rc)
+    torch.cuda.synchronize()
+    ref = _oracle(w, W, b, np.zeros(1, np.int32), np.zeros(0, np.int32))
+    assert_close(y.double().cpu().numpy(), ref, "f16", "S=0, NULL tables")
 
 
 def test_invalid_adapter_rows_get_the_base_product():

@@ -13,8 +13,8 @@ import pytest
 
 import oracle
 import workloads as wl
-from gpu_helpers import (assert_close, gpu_expand, gpu_lora_apply, gpu_shrink, to_device,
-                         torch_dtype)
+from gpu_helpers import (assert_close, gpu_expand, gpu_lora_apply, gpu_shrink, magnitude,
+                         magnitude_expand, to_device, torch_dtype)
 
 pytestmark = pytest.mark.gpu
 
@@ -36,8 +36,9 @@ def _config(key):
         i, ctl = key
         w = wl.config(i, control=ctl)
         y, v = oracle.lora_apply(w.y0, w.x, w.A, w.B, w.seg_indptr, w.adapter_ids, w.scale)
+        my, mv = magnitude(w) if w.dtype == "f32" else (None, None)
         _cache.clear()  # keep at most one full-size workload in memory
-        _cache[key] = (w, y, v)
+        _cache[key] = (w, y, v, my, mv)
     return _cache[key]
 
 
@@ -47,13 +48,28 @@ CONFIG_IDS = ["tiny", "llama7b_decode", "skewed_zipf", "skewed_control", "prefil
 
 @pytest.mark.parametrize("key", CONFIG_KEYS, ids=CONFIG_IDS)
 def test_config_all_entry_points(key):
-    w, y_ref, v_ref = _config(key)
+    w, y_ref, v_ref, my, mv = _config(key)
     d = to_device(w)
-    assert_close(gpu_lora_apply(w, d), y_ref, w.dtype, f"lora_apply {w.name}")
-    assert_close(gpu_shrink(w, d), v_ref, w.dtype, f"sgmv_shrink {w.name}")
+    assert_close(gpu_lora_apply(w, d), y_ref, w.dtype, f"lora_apply {w.name}", my)
+    assert_close(gpu_shrink(w, d), v_ref, w.dtype, f"sgmv_shrink {w.name}", mv)
     # expand alone, fed the oracle's v rounded to float32
     y_e = oracle.expand(w.y0, v_ref.astype(np.float32), w.B, w.seg_indptr, w.adapter_ids, w.scale)
-    assert_close(gpu_expand(w, v_ref, d), y_e, w.dtype, f"sgmv_expand {w.name}")
+    me = magnitude_expand(w, v_ref) if w.dtype == "f32" else None
+    assert_close(gpu_expand(w, v_ref, d), y_e, w.dtype, f"sgmv_expand {w.name}", me)
+
+
+def test_mixed_batch_all_entry_points():
+    """A serving batch of two 512-row prefill segments and 128 one-row decode
+    segments on 130 distinct adapters, every output element of every entry
+    point against the oracle."""
+    w = wl.mixed_batch(0)
+    y_ref, v_ref = oracle.lora_apply(w.y0, w.x, w.A, w.B, w.seg_indptr, w.adapter_ids, w.scale)
+    d = to_device(w)
+    print(f"mixed batch {w.name}", flush=True)
+    assert_close(gpu_lora_apply(w, d), y_ref, w.dtype, "lora_apply mixed")
+    assert_close(gpu_shrink(w, d), v_ref, w.dtype, "sgmv_shrink mixed")
+    y_e = oracle.expand(w.y0, v_ref.astype(np.float32), w.B, w.seg_indptr, w.adapter_ids, w.scale)
+    assert_close(gpu_expand(w, v_ref, d), y_e, w.dtype, "sgmv_expand mixed")
 
 
 RANDOM_CASES = [
@@ -87,11 +103,12 @@ def test_random_shapes(case):
     w = wl.small_random(zlib.crc32(repr(case).encode()), dtype, H1, H2, r, N, R, S, allow_empty=True,
                         uncovered_tail=R // 7)
     y_ref, v_ref = oracle.lora_apply(w.y0, w.x, w.A, w.B, w.seg_indptr, w.adapter_ids, w.scale)
+    my, mv = magnitude(w)
     d = to_device(w)
-    assert_close(gpu_lora_apply(w, d), y_ref, dtype, "lora_apply")
+    assert_close(gpu_lora_apply(w, d), y_ref, dtype, "lora_apply", my)
     cov = int(w.seg_indptr[-1])
     v = gpu_shrink(w, d, fill=-3.5)
-    assert_close(v[:cov], v_ref[:cov], dtype, "sgmv_shrink")
+    assert_close(v[:cov], v_ref[:cov], dtype, "sgmv_shrink", mv[:cov])
     assert np.all(v[cov:] == -3.5), "shrink wrote rows outside every segment"
 
 
@@ -253,6 +270,48 @@ def test_graph_replay_matches_eager():
         del junk
 
 
+def test_capture_without_workspace_is_refused():
+    """A capture that relies on the binding's cached workspace is refused
+    (the graph would keep a buffer the cache may replace or share); a graph
+    captured with its own workspace keeps replaying correctly after a larger
+    eager call has grown the cache."""
+    import torch
+    import segmented_gather_gemv_sgmv_amd as sg
+    w = wl.small_random(71, "f16", 1024, 1024, 16, 8, 40, 10)
+    d = to_device(w)
+    y_ref = gpu_lora_apply(w, d)
+    y = d["y0"].clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        sg.lora_apply(y, d["x"], d["A"], d["B"], d["seg"], d["ids"], w.scale)  # warm the cache
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with pytest.raises(RuntimeError, match="workspace"):
+        with torch.cuda.graph(g):
+            sg.lora_apply(y, d["x"], d["A"], d["B"], d["seg"], d["ids"], w.scale)
+    torch.cuda.synchronize()
+    ws = torch.zeros(sg.lora_apply_workspace_bytes(w.num_rows, w.num_segments, w.H1, w.H2, w.r,
+                                                   torch.float16),
+                     dtype=torch.uint8, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sg.lora_apply(y, d["x"], d["A"], d["B"], d["seg"], d["ids"], w.scale, workspace=ws)
+    big = wl.small_random(72, "f16", 4096, 4096, 16, 8, 600, 40)
+    big_ref = oracle.lora_apply(big.y0, big.x, big.A, big.B, big.seg_indptr, big.adapter_ids,
+                                big.scale)[0]
+    db = to_device(big)
+    for rep in range(3):
+        y.copy_(d["y0"])
+        g.replay()
+        yb = db["y0"].clone()
+        sg.lora_apply(yb, db["x"], db["A"], db["B"], db["seg"], db["ids"], big.scale)  # cache grows
+        torch.cuda.synchronize()
+        assert np.array_equal(y.double().cpu().numpy(), y_ref), f"replay {rep}"
+        assert_close(yb.double().cpu().numpy(), big_ref, "f16", f"eager {rep}")
+
+
 SELF_CONTAINED_CASES = {
     # MFMA row tiles, one long segment
     "skewed_control": lambda: wl.config(2, control=True),
@@ -315,7 +374,8 @@ def test_workspace_reused_across_shapes():
         sg.lora_apply(y, d["x"], d["A"], d["B"], d["seg"], d["ids"], w.scale, workspace=ws)
         torch.cuda.synchronize()
         y_ref, _ = oracle.lora_apply(w.y0, w.x, w.A, w.B, w.seg_indptr, w.adapter_ids, w.scale)
-        assert_close(y.double().cpu().numpy(), y_ref, w.dtype, w.name)
+        my, mv = magnitude(w)
+        assert_close(y.double().cpu().numpy(), y_ref, w.dtype, w.name, my)
         assert int(ws[:262144].view(torch.int32).abs().sum()) == 0
         # sgmv_shrink on the same workspace (its tile counters sit there too)
         v = torch.zeros(w.num_rows, w.r, dtype=torch.float32, device="cuda")
@@ -325,7 +385,8 @@ def test_workspace_reused_across_shapes():
         covered = np.zeros(w.num_rows, bool)
         for k in range(w.num_segments):
             covered[w.seg_indptr[k]:w.seg_indptr[k + 1]] = True
-        assert_close(v.double().cpu().numpy()[covered], v_ref[covered], w.dtype, w.name + " shrink")
+        assert_close(v.double().cpu().numpy()[covered], v_ref[covered], w.dtype, w.name + " shrink",
+                     mv[covered])
         assert int(ws[:262144].view(torch.int32).abs().sum()) == 0
 
 

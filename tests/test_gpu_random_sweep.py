@@ -11,7 +11,8 @@ import pytest
 
 import oracle
 import workloads as wl
-from gpu_helpers import assert_close, gpu_expand, gpu_lora_apply, gpu_shrink, to_device
+from gpu_helpers import (assert_close, gpu_expand, gpu_lora_apply, gpu_shrink, magnitude,
+                         magnitude_expand, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -52,15 +53,16 @@ def test_random_shape_all_entry_points(case):
     w = _draw(case)
     d = to_device(w)
     y_ref, v_ref = oracle.lora_apply(w.y0, w.x, w.A, w.B, w.seg_indptr, w.adapter_ids, w.scale)
-    assert_close(gpu_lora_apply(w, d), y_ref, w.dtype, f"lora_apply {w.name}")
+    my, mv = magnitude(w)
+    assert_close(gpu_lora_apply(w, d), y_ref, w.dtype, f"lora_apply {w.name}", my)
     covered = np.zeros(w.num_rows, bool)
     for k in range(w.num_segments):
         covered[w.seg_indptr[k]:w.seg_indptr[k + 1]] = True
     v = gpu_shrink(w, d, fill=-1.25)
-    assert_close(v[covered], v_ref[covered], w.dtype, f"sgmv_shrink {w.name}")
+    assert_close(v[covered], v_ref[covered], w.dtype, f"sgmv_shrink {w.name}", mv[covered])
     assert np.all(v[~covered] == -1.25), "shrink wrote rows outside every segment"
     y_e = oracle.expand(w.y0, v_ref.astype(np.float32), w.B, w.seg_indptr, w.adapter_ids, w.scale)
     y = gpu_expand(w, v_ref, d)
-    assert_close(y, y_e, w.dtype, f"sgmv_expand {w.name}")
+    assert_close(y, y_e, w.dtype, f"sgmv_expand {w.name}", magnitude_expand(w, v_ref))
     assert np.array_equal(y[~covered], w.y0[~covered].astype(np.float64)), \
         "expand changed rows outside every segment"

@@ -72,14 +72,17 @@ def test_group_rows_rejects_too_many_adapters():
     assert e.value.code == 4
 
 
-def _reference(w, row_ids):
+def _reference(w, row_ids, absolute=False):
     """The oracle on the batch grouped by the (pinned) oracle grouping, with
-    the rows put back in place; rows without an adapter keep y0."""
+    the rows put back in place; rows without an adapter keep y0.  With
+    ``absolute``, the oracle on the inputs' absolute values (the magnitude
+    of each element's terms)."""
+    f = np.abs if absolute else (lambda a: a)
     perm, seg, aid, count = og.group_rows(row_ids, w.num_adapters)
     perm = np.asarray(perm)
-    y_g, _ = oracle.lora_apply(w.y0[perm], w.x[perm], w.A, w.B,
+    y_g, _ = oracle.lora_apply(f(w.y0[perm]), f(w.x[perm]), f(w.A), f(w.B),
                                np.asarray(seg[:count + 1], dtype=np.int32),
-                               np.asarray(aid[:count], dtype=np.int32), w.scale)
+                               np.asarray(aid[:count], dtype=np.int32), f(w.scale))
     y = np.empty_like(y_g)
     y[perm] = y_g
     return y
@@ -99,6 +102,7 @@ def test_lora_apply_from_per_row_ids(dtype, H1, H2, r, N, R):
     row_ids = rng.integers(-1, N + 1, size=R)
     row_ids[: R // 3] = np.sort(row_ids[: R // 3])  # some long runs too
     y_ref = _reference(w, row_ids.tolist())
+    mag = _reference(w, row_ids.tolist(), absolute=True)
     d = to_device(w)
     rid = _dev(row_ids)
 
@@ -106,7 +110,7 @@ def test_lora_apply_from_per_row_ids(dtype, H1, H2, r, N, R):
     y = d["y0"].clone()
     sg.lora_apply(y, d["x"], d["A"], d["B"], seg, ids, w.scale)
     torch.cuda.synchronize()
-    assert_close(y.double().cpu().numpy(), y_ref, dtype, "run table")
+    assert_close(y.double().cpu().numpy(), y_ref, dtype, "run table", mag)
 
     perm, seg, ids, _ = sg.group_rows(rid, N)
     p = perm.long()
@@ -115,12 +119,12 @@ def test_lora_apply_from_per_row_ids(dtype, H1, H2, r, N, R):
     y = torch.empty_like(yg)
     y[p] = yg
     torch.cuda.synchronize()
-    assert_close(y.double().cpu().numpy(), y_ref, dtype, "grouped table")
+    assert_close(y.double().cpu().numpy(), y_ref, dtype, "grouped table", mag)
     invalid = (row_ids < 0) | (row_ids >= N)
     assert np.array_equal(y.double().cpu().numpy()[invalid], w.y0[invalid].astype(np.float64))
 
 
-@pytest.mark.parametrize("group", [False, True], ids=["runs", "grouped"])
+@pytest.mark.parametrize("group", [False, True, "auto"], ids=["runs", "grouped", "auto"])
 def test_lora_linear_module(group):
     """LoRALinear = torch's dense linear for the base product plus the SGMV
     add-on for per-row adapters: its output equals the oracle's add-on

@@ -186,6 +186,23 @@ def mlp_up_decode(seed=0) -> Workload:
                          lengths, ids, 0.5, rng=rng)
 
 
+def mixed_batch(seed=0, long_rows=(512, 512), short=128, H=4096, r=16, dtype="f16",
+                num_adapters=256) -> Workload:
+    """A serving batch that mixes prefill and decode requests: segments of
+    ``long_rows`` rows (prefill prompts) and ``short`` one-row segments
+    (decode steps), each segment on its own adapter, the adapters drawn
+    without replacement from a stack of ``num_adapters``, the segment order
+    shuffled.  4096 -> 4096, r=16, fp16, s=2 by default (two 512-row
+    segments plus 128 one-row segments: 1152 rows over 130 adapters)."""
+    rng = np.random.default_rng(seed)
+    lengths = np.array(list(long_rows) + [1] * short, dtype=np.int64)
+    order = rng.permutation(len(lengths))
+    lengths = lengths[order]
+    ids = rng.choice(num_adapters, size=len(lengths), replace=False).astype(np.int32)
+    name = f"mixed_{H}_r{r}_{'+'.join(map(str, long_rows))}+{short}x1"
+    return make_workload(name, dtype, H, H, r, num_adapters, lengths, ids, 32.0 / r, rng=rng)
+
+
 CONFIGS = {
     0: tiny,
     1: llama7b_decode,
