@@ -98,7 +98,9 @@ typedef enum {
     SGMV_ERR_UNSUPPORTED = 4,  /* sizes beyond what the kernels index (>2^31)   */
     SGMV_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than required       */
     SGMV_ERR_HIP = 6,          /* a HIP launch reported an error                */
-    SGMV_ERR_BAD_SEGMENTS = 7  /* (validator only) malformed segment table      */
+    SGMV_ERR_BAD_SEGMENTS = 7, /* (validator only) malformed segment table      */
+    SGMV_ERR_SCRATCH = 8       /* lora_apply_noalloc: the call needs more than  */
+                               /* SGMV_NOALLOC_SCRATCH_BYTES of scratch         */
 } sgmv_status_t;
 
 /* Version of this ABI (SGMV_ABI_VERSION of the library that was loaded). */
@@ -158,6 +160,35 @@ int lora_apply(void* y, const void* x, const void* A_stack, const void* B_stack,
                int32_t num_segments, int32_t num_rows, int32_t num_adapters,
                int32_t H1, int32_t H2, int32_t r, float scale, int32_t dtype,
                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * lora_apply for callers that cannot allocate memory -- code being captured
+ * into a HIP graph, tight serving loops, harnesses that forbid hipMalloc:
+ * the same computation, kernels and results as lora_apply (bit for bit),
+ * with no workspace argument.  Its scratch is a static device array inside
+ * the library, SGMV_NOALLOC_SCRATCH_BYTES per GPU, held from the first call
+ * on a GPU until the process ends.  The call allocates nothing: no hipMalloc,
+ * no hipFree, no allocating library routine.
+ *
+ * Limit: a call whose lora_apply_workspace_bytes(...) exceeds
+ * SGMV_NOALLOC_SCRATCH_BYTES returns SGMV_ERR_SCRATCH before enqueueing
+ * anything (use lora_apply with a workspace of that size instead).
+ *
+ * The scratch is shared by every call on one GPU and keeps what the last
+ * call left there: calls that may overlap on one GPU (different streams,
+ * different host threads without ordering) race and must not be made.
+ * Its synchronisation counters are zero when the library is loaded (static
+ * storage) and every call leaves them zero; the first call on a GPU made
+ * outside a graph capture also clears them with a small kernel on `stream`.
+ * The current device must be the GPU that `stream` belongs to.  Arguments,
+ * layout and the other errors are those of lora_apply.
+ */
+#define SGMV_NOALLOC_SCRATCH_BYTES (16u << 20)
+int lora_apply_noalloc(void* y, const void* x, const void* A_stack, const void* B_stack,
+                       const int32_t* seg_indptr, const int32_t* adapter_ids,
+                       int32_t num_segments, int32_t num_rows, int32_t num_adapters,
+                       int32_t H1, int32_t H2, int32_t r, float scale, int32_t dtype,
+                       void* stream);
 
 /*
  * Several LoRA add-ons over one batch -- e.g. the q, k, v and o projections

@@ -32,8 +32,9 @@ SGMV_MAX_RANK = 128
 STATUS = {
     0: "SGMV_OK", 1: "SGMV_ERR_NULL_PTR", 2: "SGMV_ERR_BAD_SHAPE", 3: "SGMV_ERR_BAD_DTYPE",
     4: "SGMV_ERR_UNSUPPORTED", 5: "SGMV_ERR_WORKSPACE", 6: "SGMV_ERR_HIP",
-    7: "SGMV_ERR_BAD_SEGMENTS",
+    7: "SGMV_ERR_BAD_SEGMENTS", 8: "SGMV_ERR_SCRATCH",
 }
+SGMV_NOALLOC_SCRATCH_BYTES = 16 << 20
 SGMV_MAX_PROBLEMS = 8
 
 
@@ -58,6 +59,8 @@ ABI = [
     ("lora_apply_workspace_bytes", _sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     ("lora_apply", ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                   _i32, _f32, _i32, _vp, _sz, _vp]),
+    ("lora_apply_noalloc", ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                          _i32, _i32, _f32, _i32, _vp]),
     ("sgmv_set_fused_wait", ctypes.c_int, [ctypes.c_double]),
     ("sgmv_validate_segments", ctypes.c_int, [_vp, _vp, _i32, _i32, _i32]),
     ("sgmv_build_segments", ctypes.c_int, [_vp, _i32, _i32, _vp, _vp, _vp, _vp]),
@@ -273,6 +276,31 @@ def lora_apply(y, x, A_stack, B_stack, seg_indptr, adapter_ids, scale=1.0, works
     return y
 
 
+def lora_apply_noalloc(y, x, A_stack, B_stack, seg_indptr, adapter_ids, scale=1.0):
+    """lora_apply without a workspace argument: the library's static per-GPU
+    scratch (SGMV_NOALLOC_SCRATCH_BYTES) serves every call, and nothing is
+    allocated, so the call may be captured in a graph as it stands.  Calls
+    that may overlap on one GPU race on that scratch."""
+    dev = x.device
+    _need(x, "x", dev, None, 2)
+    _need(y, "y", dev, x.dtype, 2)
+    _need(A_stack, "A_stack", dev, x.dtype, 3)
+    _need(B_stack, "B_stack", dev, x.dtype, 3)
+    S = _segments(seg_indptr, adapter_ids, dev)
+    R, H1 = x.shape
+    N, H1a, r = A_stack.shape
+    Nb, rb, H2 = B_stack.shape
+    if H1a != H1 or Nb != N or rb != r or tuple(y.shape) != (R, H2):
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)}, y {tuple(y.shape)}, "
+                         f"A_stack {tuple(A_stack.shape)}, B_stack {tuple(B_stack.shape)}")
+    _check(lib().lora_apply_noalloc(y.data_ptr(), x.data_ptr(), A_stack.data_ptr(),
+                                    B_stack.data_ptr(), seg_indptr.data_ptr(),
+                                    adapter_ids.data_ptr(), S, R, N, H1, H2, r, float(scale),
+                                    dtype_code(x.dtype), _stream_ptr(dev)),
+           "lora_apply_noalloc")
+    return y
+
+
 def lora_linear_workspace_bytes(num_rows, num_segments, H1, H2, r, dtype) -> int:
     return int(lib().lora_linear_workspace_bytes(num_rows, num_segments, H1, H2, r,
                                                  dtype_code(dtype)))
@@ -477,6 +505,6 @@ __all__ = [
     "build_segments", "group_rows", "lora_apply_multi", "lora_apply_multi_workspace_bytes",
     "load_adapter",
     "LoraProblem",
-    "lora_apply", "sgmv_shrink", "sgmv_expand", "lora_apply_workspace_bytes",
+    "lora_apply", "lora_apply_noalloc", "sgmv_shrink", "sgmv_expand", "lora_apply_workspace_bytes",
     "shrink_workspace_bytes", "validate_segments", "set_fused_wait", "lib", "SGMVError", "ABI", "LIBRARY",
 ]

@@ -11,6 +11,7 @@
 
 #include <atomic>
 #include <cstring>
+#include <mutex>
 #include <tuple>
 #include <type_traits>
 #include <utility>
@@ -547,6 +548,66 @@ void launch_linear_tiled(void* y, const void* x, const void* W, const void* bias
            (int)lp.tiles);
 }
 
+// -- scratch of lora_apply_noalloc ------------------------------------------
+// A file-scope device array: each GPU the library runs on holds its own copy
+// from the moment the library's code is loaded there until the process ends.
+// In host code `scratch` names a host-side stand-in, not device memory, so
+// host code never passes it to a kernel or a copy: the device address comes
+// from hipGetSymbolAddress, once per device, and is kept in g_scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[SGMV_NOALLOC_SCRATCH_BYTES];
+static_assert(SGMV_NOALLOC_SCRATCH_BYTES > kCounterBytes, "scratch must hold the counters");
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+bool g_scratch_cleared[kMaxDevices] = {};
+
+__global__ __launch_bounds__(256) void zero_ints_kernel(int* __restrict__ p, int n) {
+    const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (i < n) p[i] = 0;
+}
+
+// The current device's scratch address (looked up on its first use), with
+// the counter region cleared by a kernel on `st` at the first call on the
+// device that is not being captured (static storage is zero already; this
+// makes no assumption about it).  Allocates nothing.
+int device_scratch(hipStream_t st, void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        t_last = e;
+        return SGMV_ERR_HIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return SGMV_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            t_last = e != hipSuccess ? e : hipErrorInvalidSymbol;
+            return SGMV_ERR_HIP;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    if (!g_scratch_cleared[dev]) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        e = hipStreamIsCapturing(st, &cs);
+        if (e != hipSuccess) {
+            t_last = e;
+            return SGMV_ERR_HIP;
+        }
+        if (cs == hipStreamCaptureStatusNone) {
+            launch(&zero_ints_kernel, dim3((kCounterInts + 255) / 256), dim3(256), st,
+                   (int*)g_scratch_ptr[dev], kCounterInts);
+            const int rc = launch_status();
+            if (rc != SGMV_OK) return rc;
+            g_scratch_cleared[dev] = true;
+        }
+    }
+    *out = g_scratch_ptr[dev];
+    return SGMV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -565,6 +626,9 @@ const char* sgmv_status_string(int status) {
         case SGMV_ERR_WORKSPACE: return "workspace missing or too small";
         case SGMV_ERR_HIP: return "HIP launch error";
         case SGMV_ERR_BAD_SEGMENTS: return "malformed segment table";
+        case SGMV_ERR_SCRATCH:
+            return "the call needs more scratch than lora_apply_noalloc holds "
+                   "(SGMV_NOALLOC_SCRATCH_BYTES); use lora_apply with a workspace";
         default: return "unknown status";
     }
 }
@@ -796,6 +860,25 @@ int lora_apply(void* y, const void* x, const void* A_stack, const void* B_stack,
                             num_segments, num_rows, num_adapters, r, H2, scale, p, st);
     });
     return launch_status();
+}
+
+int lora_apply_noalloc(void* y, const void* x, const void* A_stack, const void* B_stack,
+                       const int32_t* seg_indptr, const int32_t* adapter_ids,
+                       int32_t num_segments, int32_t num_rows, int32_t num_adapters, int32_t H1,
+                       int32_t H2, int32_t r, float scale, int32_t dtype, void* stream) {
+    // lora_apply's checks, in its order, before the scratch is touched.
+    int rc = check_common(num_segments, num_rows, num_adapters, r, dtype);
+    if (rc != SGMV_OK) return rc;
+    if (H1 < 1 || H2 < 1) return SGMV_ERR_BAD_SHAPE;
+    if (num_rows == 0 || num_segments == 0) return SGMV_OK;
+    if (!y || !x || !A_stack || !B_stack || !seg_indptr || !adapter_ids) return SGMV_ERR_NULL_PTR;
+    const size_t need = lora_apply_workspace_bytes(num_rows, num_segments, H1, H2, r, dtype);
+    if (need > (size_t)SGMV_NOALLOC_SCRATCH_BYTES) return SGMV_ERR_SCRATCH;
+    void* ws = nullptr;
+    if ((rc = device_scratch((hipStream_t)stream, &ws)) != SGMV_OK) return rc;
+    return lora_apply(y, x, A_stack, B_stack, seg_indptr, adapter_ids, num_segments, num_rows,
+                      num_adapters, H1, H2, r, scale, dtype, ws,
+                      (size_t)SGMV_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 // -- several add-ons in one launch ------------------------------------------

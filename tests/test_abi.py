@@ -42,7 +42,7 @@ def test_abi_version_matches_header(lib):
 
 
 def test_status_strings(lib):
-    for code in range(0, 8):
+    for code in range(0, 9):
         s = lib.sgmv_status_string(code)
         assert isinstance(s, bytes) and len(s) > 0
     assert lib.sgmv_status_string(0) == b"ok"
@@ -222,3 +222,34 @@ def test_lora_linear_workspace_sizes(lib):
     assert (lib.lora_linear_workspace_bytes(64, 64, 4096, 4096, 16, 1)
             > lib.lora_apply_workspace_bytes(64, 64, 4096, 4096, 16, 1))
     assert lib.lora_linear_workspace_bytes(16, 4, 256, 256, 0, 1) == 0
+
+
+def _noalloc(lib, **kw):
+    a = dict(y=FAKE, x=FAKE, A=FAKE, B=FAKE, seg=FAKE, ids=FAKE, S=4, R=16, N=4, H1=256, H2=256,
+             r=8, scale=1.0, dtype=0, stream=None)
+    a.update(kw)
+    return lib.lora_apply_noalloc(a["y"], a["x"], a["A"], a["B"], a["seg"], a["ids"], a["S"],
+                                  a["R"], a["N"], a["H1"], a["H2"], a["r"], a["scale"],
+                                  a["dtype"], a["stream"])
+
+
+def test_noalloc_rejects_bad_arguments_and_oversized_calls(lib):
+    """The allocation-free entry point returns lora_apply's errors, and
+    SGMV_ERR_SCRATCH for a call whose workspace would exceed the static
+    scratch, all before it touches the device."""
+    assert _noalloc(lib, dtype=7) == 3
+    assert _noalloc(lib, r=0) == 2
+    assert _noalloc(lib, H2=0) == 2
+    for p in ("y", "x", "A", "B", "seg", "ids"):
+        assert _noalloc(lib, **{p: None}) == 1, p
+    assert _noalloc(lib, R=0) == 0 and _noalloc(lib, S=0) == 0  # no-ops
+    m = re.search(r"#define\s+SGMV_NOALLOC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)",
+                  open(HEADER).read())
+    limit = int(m.group(1)) << int(m.group(2))
+    assert limit == sg.SGMV_NOALLOC_SCRATCH_BYTES
+    # a prefill-sized call at a large rank needs more than the scratch holds
+    R, S, H, r = 65536, 16, 8192, 128
+    need = lib.lora_apply_workspace_bytes(R, S, H, H, r, 1)
+    assert need > limit
+    assert _noalloc(lib, R=R, S=S, H1=H, H2=H, r=r, dtype=1) == 8
+    assert b"lora_apply_noalloc" in lib.sgmv_status_string(8)
