@@ -9,6 +9,7 @@
 
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstring>
 #include <mutex>
@@ -23,6 +24,7 @@
 #include "sgmv_mfma.hpp"
 #include "sgmv_segments.hpp"
 #include "sgmv_linear.hpp"
+#include "sgmv_mixed.hpp"
 
 namespace {
 
@@ -254,6 +256,211 @@ MfmaSplitPlan make_mfma_split_plan(const MfmaPlan& mp, int H1, int H2, int r) {
     sp.ok = sp.grid_shrink <= kMaxGrid && sp.grid_expand <= kMaxGrid;
     return sp;
 }
+
+// -- per-segment path choice (sgmv_mixed.hpp) -----------------------------------
+// Every workgroup of the mixed kernels classifies the segments itself: long
+// (>= TH rows: 16-row MFMA tiles), short (2..TH-1 rows: 4-row vector tiles),
+// single (one row: one-row vector tiles).  The host only picks the chunk
+// sizes of each class and sizes the grid by the largest item count any
+// table of this length could need.
+constexpr long long kMixedBudget = 1024;  // one resident round: four workgroups per CU
+constexpr int kMixedMaxSplit = 16;        // one-launch H1 chunks: one batch of partial loads
+
+struct MixedShape {
+    bool ok;               // the mixed kernels serve these shapes
+    bool has_long, has_short;
+    int TH;                // rows from which a segment is long
+    int T[3];              // tile rows: long, short, single
+    int cw[3], unit[3], hmax[3];  // columns per expand item, H1 unit, rows per LDS chunk (0: any)
+    int e, r;
+};
+
+MixedShape mixed_shape(int H1, int H2, int r, int dtype) {
+    MixedShape m{};
+    if (!vec_rank(dtype, r)) return m;
+    const int vec = vec_width(dtype);
+    if (H2 % vec != 0) return m;
+    const bool mfma_rank = dtype != SGMV_F32 && r >= 16;
+    if (mfma_rank && (H1 % 8 != 0 || H2 % 8 != 0)) return m;  // the per-call kernels serve these
+    m.e = elem_bytes(dtype);
+    m.r = r;
+    m.has_long = mfma_rank;
+    m.has_short = !mfma_rank || r >= 64;
+    m.TH = !m.has_long ? 0x7FFFFFFF : (m.has_short ? 16 : 2);
+    const int vunit = kMixedThreads / (r / vec);
+    m.T[0] = 16;
+    m.cw[0] = std::min(512, 8192 / r);
+    m.unit[0] = 128;
+    m.hmax[0] = std::max(128, 8192 / r);  // MfmaTile's LDS chunk of A
+    m.T[1] = 4;
+    m.T[2] = 1;
+    for (int c = 1; c < 3; ++c) {
+        m.cw[c] = kMixedThreads * vec;
+        m.unit[c] = vunit;
+        m.hmax[c] = 0;
+    }
+    m.ok = true;
+    return m;
+}
+
+// An upper bound, over every table of S segments on R rows, of
+// sum over segments of q[class] * (tiles of the segment).  A segment of n
+// rows in a class of tile height T has ceil(n / T) <= 1 + (n - 1) / T
+// tiles, linear in n within the class's range of lengths, so the count is
+// a linear program over how many segments of each length there are, with
+// two constraints (at most S segments, at most R rows).  Its optimum uses at
+// most two lengths, and within a class only the ends of its range of
+// lengths matter; the bound is that optimum over all pairs of such ends.
+long long mixed_bound(long long R, long long S, const MixedShape& ms, const long long (&q)[3]) {
+    struct End { double n, v; };
+    End ends[6];
+    int ne = 0;
+    auto add = [&](int c, long long n) {
+        if (n < 1 || n > R) return;
+        ends[ne++] = End{(double)n, (double)q[c] * (1.0 + (double)(n - 1) / (double)ms.T[c])};
+    };
+    add(2, 1);
+    if (ms.has_short) {
+        add(1, 2);
+        add(1, std::min<long long>(ms.TH - 1, R));
+    }
+    if (ms.has_long) {
+        add(0, ms.TH);
+        add(0, R);
+    }
+    double best = 0.0;
+    for (int a = 0; a < ne; ++a) {
+        for (int b = a; b < ne; ++b) {
+            const End& A = ends[a];
+            const End& B = ends[b];
+            // one length alone
+            best = std::max(best, std::min((double)S, (double)R / A.n) * A.v);
+            best = std::max(best, std::min((double)S, (double)R / B.n) * B.v);
+            // both, with both constraints tight
+            if (B.n != A.n) {
+                const End& lo = A.n < B.n ? A : B;
+                const End& hi = A.n < B.n ? B : A;
+                const double xh = ((double)R - lo.n * (double)S) / (hi.n - lo.n);
+                const double xl = (double)S - xh;
+                if (xh >= 0.0 && xl >= 0.0) best = std::max(best, xl * lo.v + xh * hi.v);
+            }
+        }
+    }
+    return (long long)best + 1;
+}
+
+// Chunk sizes for a target of `tb` bytes per shrink item: an item of a
+// tall tile reads its rows of A and, for each of its T rows, the same
+// stretch of x; a one-row item reads its rows of A (its stretch of x, 1/r
+// of that, stays out of the count so that power-of-two targets give
+// power-of-two chunks).  One-launch long chunks stay within one LDS chunk
+// of A; two-launch ones may span several (summed in order).
+MixedSplit mixed_split(const MixedShape& ms, long long tb, int H1, int H2, bool one_launch) {
+    MixedSplit sp{};
+    for (int c = 0; c < 3; ++c) {
+        const int unit = ms.unit[c];
+        const long long per_row = (long long)(ms.r + (ms.T[c] > 1 ? ms.T[c] : 0)) * ms.e;
+        long long hh = tb / per_row / unit * unit;
+        if (hh < unit) hh = unit;
+        if (ms.hmax[c] > 0 && one_launch && hh > ms.hmax[c]) hh = ms.hmax[c];
+        const long long hcap = ((long long)H1 + unit - 1) / unit * unit;
+        if (hh > hcap) hh = hcap;
+        const long long kk = (H1 + hh - 1) / hh;
+        hh = ((H1 + kk - 1) / kk + unit - 1) / unit * unit;
+        sp.k[c] = (int)kk;
+        sp.h[c] = (int)hh;
+        sp.c[c] = (H2 + ms.cw[c] - 1) / ms.cw[c];
+    }
+    return sp;
+}
+
+struct MixedPlan {
+    bool ok;
+    bool two;              // two launches (else one)
+    MixedSplit one, two_sp;
+    long long grid_one, grid_shrink, grid_expand;
+    long long tiles;       // bound on the tiles (tile counters)
+    int kmax;              // partial chunks the workspace holds (either form)
+};
+
+// Pure function of the shapes: the one-launch form with the finest chunks
+// (at most kMixedMaxSplit per tile) whose items fit one resident round --
+// the coarsest if none do -- unless even that needs more than two rounds or
+// more tiles than there are counters; then the two-launch form, whose
+// shrink launch takes the finest chunks that fit two rounds.
+MixedPlan make_mixed_plan(const MixedShape& ms, int R, int S, int H1, int H2) {
+    MixedPlan p{};
+    if (!ms.ok || S < 1 || R < 1 || S > kMixedMaxSegments) return p;
+    const long long ones[3] = {1, 1, 1};
+    p.tiles = mixed_bound(R, S, ms, ones);
+    static const long long kTargets[] = {4096, 8192, 16384, 32768, 65536, 131072, 262144};
+    bool found = false;
+    for (int i = 0; i < 5 && !found; ++i) {
+        p.one = mixed_split(ms, kTargets[i], H1, H2, true);
+        const long long q[3] = {p.one.k[0] + p.one.c[0], p.one.k[1] + p.one.c[1],
+                                p.one.k[2] + p.one.c[2]};
+        p.grid_one = mixed_bound(R, S, ms, q);
+        int kmx = 0;
+        for (int c = 0; c < 3; ++c) kmx = std::max(kmx, p.one.k[c]);
+        found = p.grid_one <= kMixedBudget && kmx <= kMixedMaxSplit;
+    }
+    p.two = p.grid_one > 2 * kMixedBudget || p.tiles > kCounterSlots;
+    found = false;
+    for (int i = 0; i < 7 && !found; ++i) {
+        p.two_sp = mixed_split(ms, kTargets[i], H1, H2, false);
+        const long long qk[3] = {p.two_sp.k[0], p.two_sp.k[1], p.two_sp.k[2]};
+        p.grid_shrink = mixed_bound(R, S, ms, qk);
+        found = p.grid_shrink <= 2 * kMixedBudget;
+    }
+    const long long qc[3] = {p.two_sp.c[0], p.two_sp.c[1], p.two_sp.c[2]};
+    p.grid_expand = mixed_bound(R, S, ms, qc);
+    p.kmax = 0;
+    bool fits = true;
+    for (int c = 0; c < 3; ++c) {
+        p.kmax = std::max(p.kmax, std::max(p.one.k[c], p.two_sp.k[c]));
+        fits = fits && p.one.k[c] < (1 << 16) && p.one.c[c] < (1 << 15) && p.two_sp.k[c] >= 1;
+    }
+    p.ok = fits && p.grid_one <= kMaxGrid && p.grid_shrink <= kMaxGrid &&
+           p.grid_expand <= kMaxGrid;
+    return p;
+}
+
+// Calls f(DT{}, integral_constant<R>{}, LongP{}, ShortP{}, SingleP{}) for the
+// mixed kernels of the dtype and rank (the classes as mixed_shape defines them).
+template <typename F>
+void with_mixed(int dtype, int r, F&& f) {
+    auto by_rank = [&](auto dt) {
+        using DT = decltype(dt);
+        auto go = [&](auto rank) {
+            constexpr int R = decltype(rank)::value;
+            using G = VecTile<DT, R, 1>;
+            if constexpr (!std::is_same<DT, F32>::value && R >= 64)
+                f(dt, rank, MfmaTile<DT, R>{}, ShortTile<DT, R>{}, G{});
+            else if constexpr (!std::is_same<DT, F32>::value && R >= 16)
+                f(dt, rank, MfmaTile<DT, R>{}, NoTile<DT>{}, G{});
+            else
+                f(dt, rank, NoTile<DT>{}, ShortTile<DT, R>{}, G{});
+        };
+        switch (r) {
+            case 4:
+                if constexpr (DT::kVec == 4) go(std::integral_constant<int, 4>{});
+                break;
+            case 8: go(std::integral_constant<int, 8>{}); break;
+            case 16: go(std::integral_constant<int, 16>{}); break;
+            case 32: go(std::integral_constant<int, 32>{}); break;
+            case 64: go(std::integral_constant<int, 64>{}); break;
+            default: go(std::integral_constant<int, 128>{}); break;
+        }
+    };
+    switch (dtype) {
+        case SGMV_F32: by_rank(F32{}); break;
+        case SGMV_F16: by_rank(F16{}); break;
+        default: by_rank(BF16{}); break;
+    }
+}
+
+// Whether the mixed kernels take a call (shapes; alignment is the caller's).
+bool mixed_takes(const MixedShape& ms, int S) { return ms.ok && S <= kMixedMaxSegments; }
 
 // Calls f(DT{}, integral_constant<R>) for the MFMA tile kernels' dtypes
 // (fp16, bf16) and ranks (16, 32, 64, 128); the caller has checked both.
@@ -637,7 +844,16 @@ size_t sgmv_shrink_workspace_bytes(int32_t num_rows, int32_t num_segments, int32
                                    int32_t dtype) {
     if (check_common(num_segments, num_rows, 0, r, dtype) != SGMV_OK || H1 < 1) return 0;
     const Plan p = make_plan(num_rows, num_segments, H1, r, dtype);
-    return p.ksplit > 1 ? kCounterBytes + partial_bytes(p, num_rows, r) : 0;
+    size_t need = p.ksplit > 1 ? kCounterBytes + partial_bytes(p, num_rows, r) : 0;
+    const MixedShape ms = mixed_shape(H1, 8, r, dtype);
+    if (mixed_takes(ms, num_segments)) {
+        const MixedPlan xp = make_mixed_plan(ms, num_rows, num_segments, H1, 8);
+        const int k = std::max(std::max(xp.two_sp.k[0], xp.two_sp.k[1]), xp.two_sp.k[2]);
+        if (xp.ok && k > 1 && xp.tiles <= kCounterSlots)
+            need = std::max(need, kCounterBytes + (size_t)k * (size_t)num_rows * (size_t)r *
+                                                      sizeof(float));
+    }
+    return need;
 }
 
 size_t lora_apply_workspace_bytes(int32_t num_rows, int32_t num_segments, int32_t H1, int32_t H2,
@@ -651,6 +867,11 @@ size_t lora_apply_workspace_bytes(int32_t num_rows, int32_t num_segments, int32_
     if (mp.ok && mp.ksplit > k) k = mp.ksplit;
     const MfmaSplitPlan sp = make_mfma_split_plan(mp, H1, H2, r);
     if (sp.ok && sp.ksplit > k) k = sp.ksplit;
+    const MixedShape ms = mixed_shape(H1, H2, r, dtype);
+    if (mixed_takes(ms, num_segments)) {
+        const MixedPlan xp = make_mixed_plan(ms, num_rows, num_segments, H1, H2);
+        if (xp.ok && xp.kmax > k) k = xp.kmax;
+    }
     return kCounterBytes + (size_t)k * (size_t)num_rows * (size_t)r * sizeof(float);
 }
 
@@ -668,6 +889,45 @@ int sgmv_shrink(float* v, const void* x, const void* A_stack, const int32_t* seg
     const size_t need = p.ksplit > 1 ? kCounterBytes + partial_bytes(p, num_rows, r) : 0;
     if (need > 0 && (!workspace || workspace_bytes < need)) return SGMV_ERR_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
+    // The path chosen per segment (sgmv_mixed.hpp), the shrink half of the
+    // two-launch form.  With a split H1, each tile's last workgroup reduces
+    // the partials into v in-kernel (tile counters at the start of the
+    // workspace); calls whose tiles could outnumber the counters keep the
+    // per-call kernels.
+    {
+        const MixedShape ms = mixed_shape(H1, 8, r, dtype);
+        const MixedPlan xp = mixed_takes(ms, num_segments)
+                                 ? make_mixed_plan(ms, num_rows, num_segments, H1, 8)
+                                 : MixedPlan{};
+        const int k = std::max(std::max(xp.two_sp.k[0], xp.two_sp.k[1]), xp.two_sp.k[2]);
+        if (xp.ok && (k == 1 || xp.tiles <= kCounterSlots) && aligned16(A_stack) &&
+            (!ms.has_long || aligned16(x))) {
+            {
+                const MixedSplit& sp = xp.two_sp;
+                const size_t need_m = k > 1 ? kCounterBytes + (size_t)k * (size_t)num_rows *
+                                                                  (size_t)r * sizeof(float)
+                                            : 0;
+                if (need_m > 0 && (!workspace || workspace_bytes < need_m))
+                    return SGMV_ERR_WORKSPACE;
+                float* part = k > 1 ? (float*)((char*)workspace + kCounterBytes) : v;
+                const bool in_kernel = k > 1;
+                with_mixed(dtype, r, [&](auto dt, auto rank, auto lp, auto sp_, auto gp) {
+                    using DT = decltype(dt);
+                    using T = typename DT::storage;
+                    constexpr int R = decltype(rank)::value;
+                    using LP = decltype(lp);
+                    using SP = decltype(sp_);
+                    using GP = decltype(gp);
+                    launch(&shrink_mixed_kernel<DT, R, LP, SP, GP>, dim3((unsigned)xp.grid_shrink),
+                           dim3(kMixedThreads), st, (const T*)x, (const T*)A_stack, seg_indptr,
+                           adapter_ids, num_segments, num_rows, num_adapters, H1, part, sp,
+                           in_kernel ? v : (float*)nullptr, in_kernel ? (int*)workspace : nullptr,
+                           kCounterStride);
+                });
+                return launch_status();
+            }
+        }
+    }
     float* out = p.ksplit > 1 ? (float*)((char*)workspace + kCounterBytes) : v;
     const long long stride = (long long)num_rows * r;
     // Row-heavy calls: 16-row MFMA tiles over the same H1 ranges (each
@@ -731,6 +991,29 @@ int sgmv_expand(void* y, const float* v, const void* B_stack, const int32_t* seg
     const Plan p = make_plan(num_rows, num_segments, 1, r, dtype);
     if (!grid_fits(p, H2)) return SGMV_ERR_UNSUPPORTED;
     hipStream_t st = (hipStream_t)stream;
+    // The path chosen per segment (sgmv_mixed.hpp), the expand half of the
+    // two-launch form, v read as the single partial of every row.
+    {
+        const MixedShape ms = mixed_shape(8, H2, r, dtype);
+        if (mixed_takes(ms, num_segments) && aligned16(B_stack) && aligned16(y)) {
+            const MixedPlan xp = make_mixed_plan(ms, num_rows, num_segments, 8, H2);
+            if (xp.ok) {
+                with_mixed(dtype, r, [&](auto dt, auto rank, auto lp, auto sp_, auto gp) {
+                    using DT = decltype(dt);
+                    using T = typename DT::storage;
+                    constexpr int R = decltype(rank)::value;
+                    using LP = decltype(lp);
+                    using SP = decltype(sp_);
+                    (void)gp;
+                    launch(&expand_mixed_kernel<DT, R, LP, SP, SplitSingle<DT, R>>, dim3((unsigned)xp.grid_expand),
+                           dim3(kMixedThreads), st, (T*)y, (const T*)B_stack, seg_indptr,
+                           adapter_ids, num_segments, num_rows, num_adapters, H2, scale, v,
+                           xp.two_sp, 1, 1, 1);
+                });
+                return launch_status();
+            }
+        }
+    }
     // Row-heavy calls: 16-row MFMA tiles, v read as the single "partial".
     const MfmaPlan mp = make_mfma_plan(num_rows, num_segments, 8, H2, r, dtype);
     const long long mslots = mp.slots_a + mp.slots_b;
@@ -777,6 +1060,43 @@ int lora_apply(void* y, const void* x, const void* A_stack, const void* B_stack,
     const double wait_s = fused_wait_seconds();
     const long long wait =
         wait_s < 1e-300 ? -1 : (long long)(wait_s * (double)wall_ticks_per_second());
+    // The path chosen per segment (sgmv_mixed.hpp): one launch, or a shrink
+    // launch and an expand launch for calls beyond two resident rounds.
+    {
+        const MixedShape ms = mixed_shape(H1, H2, r, dtype);
+        if (mixed_takes(ms, num_segments) && aligned && (!ms.has_long || aligned16(x))) {
+            const MixedPlan xp = make_mixed_plan(ms, num_rows, num_segments, H1, H2);
+            if (xp.ok) {
+                with_mixed(dtype, r, [&](auto dt, auto rank, auto lp, auto sp_, auto gp) {
+                    using DT = decltype(dt);
+                    using T = typename DT::storage;
+                    constexpr int R = decltype(rank)::value;
+                    using LP = decltype(lp);
+                    using SP = decltype(sp_);
+                    using GP = decltype(gp);
+                    if (!xp.two) {
+                        launch(&lora_mixed_kernel<DT, R, LP, SP, GP>, dim3((unsigned)xp.grid_one),
+                               dim3(kMixedThreads), st, (T*)y, (const T*)x, (const T*)A_stack,
+                               (const T*)B_stack, seg_indptr, adapter_ids, num_segments, num_rows,
+                               num_adapters, H1, H2, scale, part, counters, xp.one, kCounterInts,
+                               kCounterStride, wait);
+                        return;
+                    }
+                    launch(&shrink_mixed_kernel<DT, R, LP, SP, GP>, dim3((unsigned)xp.grid_shrink),
+                           dim3(kMixedThreads), st, (const T*)x, (const T*)A_stack, seg_indptr,
+                           adapter_ids, num_segments, num_rows, num_adapters, H1, part,
+                           xp.two_sp, (float*)nullptr, (int*)nullptr, 0);
+                    if (t_pending != hipSuccess) return;  // no expand over unwritten partials
+                    launch(&expand_mixed_kernel<DT, R, LP, SP, SplitSingle<DT, R>>, dim3((unsigned)xp.grid_expand),
+                           dim3(kMixedThreads), st, (T*)y, (const T*)B_stack, seg_indptr,
+                           adapter_ids, num_segments, num_rows, num_adapters, H2, scale,
+                           (const float*)part, xp.two_sp, xp.two_sp.k[0], xp.two_sp.k[1],
+                           xp.two_sp.k[2]);
+                });
+                return launch_status();
+            }
+        }
+    }
     const MfmaPlan mp = make_mfma_plan(num_rows, num_segments, H1, H2, r, dtype);
     if (mp.ok && aligned && aligned16(x) && use_mfma(num_rows, num_segments)) {
         const MfmaSplitPlan sp = make_mfma_split_plan(mp, H1, H2, r);

@@ -181,18 +181,20 @@ __device__ __forceinline__ bool wait_for_producers(int* cnt, int ksplit, long lo
 }
 
 // Sum of the ksplit published chunk partials p[0], p[stride], ... in chunk
-// order, read with agent-scope loads (batches of 8 in flight).
+// order, read with agent-scope loads (batches of 16 in flight: each batch
+// is one dependent round trip on the expand's critical path).
 __device__ __forceinline__ float sum_partials_coherent(float* p, long long stride, int ksplit) {
+    constexpr int kBatch = 16;
     float sum = 0.f;
-    for (int p0 = 0; p0 < ksplit; p0 += 8) {
-        float tv[8];
+    for (int p0 = 0; p0 < ksplit; p0 += kBatch) {
+        float tv[kBatch];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < kBatch; ++u)
             tv[u] = (p0 + u < ksplit) ? __hip_atomic_load(p + (long long)(p0 + u) * stride,
                                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                                       : 0.f;
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < kBatch; ++u)
             if (p0 + u < ksplit) sum += tv[u];
     }
     return sum;

@@ -101,12 +101,13 @@ __device__ __forceinline__ uint4 lds_operand_tr(const uint16_t* base, int k0, in
 }
 
 
-template <int R>
+template <int R, int KC = 16384 / R>
 struct MfmaShape {
     static constexpr int kT = 16;                        // rows per tile
     static constexpr int kNT = 256;                      // threads per workgroup
     static constexpr int kNW = kNT / kWave;              // waves
-    static constexpr int kKcMax = 16384 / R;             // rows of A per chunk (32 KB of LDS)
+    static constexpr int kKcMax = KC;                    // rows of A per LDS chunk (default 32 KB)
+    static_assert(KC % (32 * kNW) == 0, "a chunk is whole K steps of every wave");
     static constexpr int kXSteps = kKcMax / (32 * kNW);  // K steps of 32 per wave and chunk
     static constexpr int kCW = (8192 / R) < 512 ? (8192 / R) : 512;  // expand columns per item
     static constexpr int kCBW = kCW / (16 * kNW);        // 16-column blocks per wave
@@ -132,13 +133,16 @@ struct MfmaShape {
 // One H1 chunk [h_lo, h_hi) of the shrink for a tile of nrows <= 16 rows,
 // reduced across the workgroup; calls emit(i, k, value) once per (i < nrows,
 // k < R) from threads tid < 16 * R.  h_lo and h_hi are multiples of 8 and
-// h_hi - h_lo <= kKcMax.  Begins and ends with the block synchronised.
-template <typename DT, int R, typename Emit>
+// h_hi - h_lo <= KC (rows of A per LDS chunk).  Begins and ends with the
+// block synchronised.
+// kRedOverA: s_red occupies the same LDS as s_a (the workgroup then waits
+// for every wave's last read of the A chunk before the sums are written).
+template <typename DT, int R, bool kRedOverA = false, int KC = 16384 / R, typename Emit>
 __device__ __forceinline__ void shrink_chunk_mfma(const typename DT::storage* __restrict__ A,
                                                   const typename DT::storage* __restrict__ xr,
                                                   int nrows, int H1, int h_lo, int h_hi,
                                                   uint16_t* s_a, float* s_red, Emit&& emit) {
-    using Sh = MfmaShape<R>;
+    using Sh = MfmaShape<R, KC>;
     using Ops = MfmaOps<DT>;
     constexpr int NB = R / 16;
     const int tid = threadIdx.x;
@@ -196,6 +200,7 @@ __device__ __forceinline__ void shrink_chunk_mfma(const typename DT::storage* __
         }
     }
     // Cross-wave sum in a fixed order.
+    if constexpr (kRedOverA) __syncthreads();
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll

@@ -315,11 +315,15 @@ def test_capture_without_workspace_is_refused():
 SELF_CONTAINED_CASES = {
     # MFMA row tiles, one long segment
     "skewed_control": lambda: wl.config(2, control=True),
-    # vector tiles of four rows
-    "mlp_up": lambda: wl.config(4),
-    # MFMA row tiles over several segments, small enough for the single kernel
-    "prefill_small": lambda: wl.small_random(31, "f16", 2048, 2048, 16, 8, 512, 8,
-                                             allow_empty=False),
+    # one-row (GEMV) tiles only: the decode batch
+    "decode": lambda: wl.config(1),
+    # both classes in one launch: MFMA tiles and one-row tiles
+    "mixed_small": lambda: wl.mixed_batch(3, long_rows=(40, 23, 2), short=60, H=2048, r=32,
+                                          dtype="bf16", num_adapters=80),
+    # float32: four-row vector tiles for the long segments, one-row tiles
+    "f32_vector_tiles": lambda: wl.make_workload("f32_mix", "f32", 1024, 768, 8, 12,
+                                                 [1, 9, 1, 1, 4, 2, 1, 7], list(range(8)),
+                                                 1.5, seed=4),
 }
 
 
