@@ -132,8 +132,12 @@ struct VecTile {
         const int h_lo = p * hps;
         const int h_hi = min(H1, h_lo + hps);
         float* out = partials + (long long)p * row_stride + (long long)t.row0 * R;
-        shrink_range(t, x, A_stack, H1, h_lo, h_hi, lds,
-                     [&](int i, int k, float v) { store_partial(&out[i * R + k], v); });
+        shrink_chunk<DT, R, NT, RB, kPG>(A_stack + (long long)t.adapter * H1 * R,
+                                         x + (long long)t.row0 * H1, t.nrows, H1, h_lo, h_hi,
+                                         reinterpret_cast<float*>(lds),
+                                         [&](int i, int k, float v) {
+                                             store_partial(&out[i * R + k], v);
+                                         });
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are acknowledged
         __syncthreads();
@@ -537,7 +541,14 @@ struct MixedScan {
     int total[3];            // tiles of each class
 };
 
-// Every thread of the block calls this.  `lds` holds 3 * NW + 8 ints.
+// LDS of the scan: per-pass wave totals of the three classes, then the
+// four ints of the found tile.
+constexpr int kMixedScanInts = kMixedPasses * 3 * (kMixedThreads / kWave) + 4;
+
+// Every thread of the block calls this.  `lds` holds kMixedScanInts ints;
+// each pass has its own slots, so one barrier per pass suffices, and the
+// found tile (the last four ints) is set to an empty tile -- no rows of
+// adapter 0 -- before that barrier.
 template <typename C>
 __device__ __forceinline__ void mixed_scan(const int* __restrict__ seg_indptr,
                                            const int* __restrict__ adapter_ids, int S,
@@ -558,9 +569,17 @@ __device__ __forceinline__ void mixed_scan(const int* __restrict__ seg_indptr,
         raw_hi[p] = seg_indptr[sc + 1];
         raw_a[p] = adapter_ids[sc];
     }
+    if (tid == 0) {
+        int* found = lds + kMixedScanInts - 4;
+        found[0] = 0;
+        found[1] = 0;
+        found[2] = 0;
+        found[3] = -1;
+    }
     int run[3] = {0, 0, 0};
 #pragma unroll
     for (int p = 0; p < kMixedPasses; ++p) {
+        int* tot_lds = lds + p * 3 * NW;
         const bool in = p * NT + tid < S;
         const int lo = min(max(raw_lo[p], 0), num_rows);
         const int hi = min(max(raw_hi[p], lo), num_rows);
@@ -582,7 +601,7 @@ __device__ __forceinline__ void mixed_scan(const int* __restrict__ seg_indptr,
         }
         if (lane == kWave - 1) {
 #pragma unroll
-            for (int c = 0; c < 3; ++c) lds[c * NW + wid] = incl[c];
+            for (int c = 0; c < 3; ++c) tot_lds[c * NW + wid] = incl[c];
         }
         __syncthreads();
 #pragma unroll
@@ -590,14 +609,13 @@ __device__ __forceinline__ void mixed_scan(const int* __restrict__ seg_indptr,
             int off = 0, tot = 0;
 #pragma unroll
             for (int w = 0; w < NW; ++w) {
-                const int v = lds[c * NW + w];
+                const int v = tot_lds[c * NW + w];
                 off += w < wid ? v : 0;
                 tot += v;
             }
             m.e[c][p] = run[c] + off + incl[c] - cnt[c];
             run[c] += tot;
         }
-        __syncthreads();
     }
 #pragma unroll
     for (int c = 0; c < 3; ++c) m.total[c] = run[c];
@@ -626,18 +644,12 @@ __device__ __forceinline__ void mixed_find_class(const MixedScan& m, int S, int 
 }
 
 // Tile t of class c (block-uniform); t must be below that class's total.
-// Every thread of the block calls this.  `found` holds 4 ints of LDS; it
-// starts as an empty tile (no rows of adapter 0), which is what a caller
-// would see if no segment held tile t.
+// Every thread of the block calls this, after mixed_scan on the same LDS
+// (`lds`); if no segment held tile t the caller would see the empty tile
+// mixed_scan left there.
 template <typename C>
-__device__ __forceinline__ Tile mixed_find(const MixedScan& m, int S, int c, int t, int* found) {
-    if (threadIdx.x == 0) {
-        found[0] = 0;
-        found[1] = 0;
-        found[2] = 0;
-        found[3] = -1;
-    }
-    __syncthreads();
+__device__ __forceinline__ Tile mixed_find(const MixedScan& m, int S, int c, int t, int* lds) {
+    int* found = lds + kMixedScanInts - 4;
     if (c == 0) mixed_find_class<C, 0>(m, S, t, found);
     else if (c == 1) mixed_find_class<C, 1>(m, S, t, found);
     else mixed_find_class<C, 2>(m, S, t, found);
@@ -685,7 +697,7 @@ __global__ __launch_bounds__(kMixedThreads, 4) void lora_mixed_kernel(
     using C = MixedClasses<LP, SP, GP>;
     constexpr int NW = kMixedThreads / kWave;
     __shared__ __align__(16) unsigned char s_mem[C::kLdsBytes];
-    __shared__ int s_scan[3 * NW + 8];
+    __shared__ int s_scan[kMixedScanInts];
     MixedScan m;
     mixed_scan<C>(seg_indptr, adapter_ids, S, num_rows, num_adapters, s_scan, m);
     const int T0 = m.total[0], T1 = m.total[1], T2 = m.total[2];
@@ -698,7 +710,7 @@ __global__ __launch_bounds__(kMixedThreads, 4) void lora_mixed_kernel(
     else if (take_item(q, T2, sp.c[2], ti, sub)) kind = 5;
     else return;  // past the real item count (block-uniform)
     const int c = kind < 3 ? kind : kind - 3;
-    const Tile t = mixed_find<C>(m, S, c, ti, s_scan + 3 * NW);
+    const Tile t = mixed_find<C>(m, S, c, ti, s_scan);
     const long long row_stride = (long long)num_rows * R;
     const int slot = c == 0 ? ti : (c == 1 ? T0 + ti : T0 + T1 + ti);
     int* cnt = &counters[(long long)slot * counter_stride];
@@ -746,7 +758,7 @@ __global__ __launch_bounds__(kMixedThreads) void shrink_mixed_kernel(
     using C = MixedClasses<LP, SP, GP>;
     constexpr int NW = kMixedThreads / kWave;
     __shared__ __align__(16) unsigned char s_mem[C::kLdsBytes];
-    __shared__ int s_scan[3 * NW + 8];
+    __shared__ int s_scan[kMixedScanInts];
     __shared__ int s_last;
     MixedScan m;
     mixed_scan<C>(seg_indptr, adapter_ids, S, num_rows, num_adapters, s_scan, m);
@@ -756,7 +768,7 @@ __global__ __launch_bounds__(kMixedThreads) void shrink_mixed_kernel(
     else if (take_item(q, T1, sp.k[1], ti, sub)) c = 1;
     else if (take_item(q, T2, sp.k[2], ti, sub)) c = 2;
     else return;
-    const Tile t = mixed_find<C>(m, S, c, ti, s_scan + 3 * NW);
+    const Tile t = mixed_find<C>(m, S, c, ti, s_scan);
     const long long row_stride = (long long)num_rows * R;
     const int slot = c == 0 ? ti : (c == 1 ? T0 + ti : T0 + T1 + ti);
     int* cnt = v_final ? &counters[(long long)slot * counter_stride] : nullptr;
@@ -782,7 +794,7 @@ __global__ __launch_bounds__(kMixedThreads, R >= 64 ? 4 : 5) void expand_mixed_k
     using C = MixedClasses<LP, SP, GP>;
     constexpr int NW = kMixedThreads / kWave;
     __shared__ __align__(16) unsigned char s_mem[C::kLdsBytes];
-    __shared__ int s_scan[3 * NW + 8];
+    __shared__ int s_scan[kMixedScanInts];
     MixedScan m;
     mixed_scan<C>(seg_indptr, adapter_ids, S, num_rows, num_adapters, s_scan, m);
     const int T0 = m.total[0], T1 = m.total[1], T2 = m.total[2];
@@ -791,7 +803,7 @@ __global__ __launch_bounds__(kMixedThreads, R >= 64 ? 4 : 5) void expand_mixed_k
     else if (take_item(q, T1, sp.c[1], ti, sub)) c = 1;
     else if (take_item(q, T2, sp.c[2], ti, sub)) c = 2;
     else return;
-    const Tile t = mixed_find<C>(m, S, c, ti, s_scan + 3 * NW);
+    const Tile t = mixed_find<C>(m, S, c, ti, s_scan);
     const long long row_stride = (long long)num_rows * R;
     if (c == 0)
         LP::expand_split(t, sub, y, B_stack, H2, scale, partials, row_stride, P_long, s_mem);
