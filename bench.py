@@ -237,10 +237,12 @@ def run_gpu(w, steps: int, warmup: int, device="cuda:0", row_ids=None, projectio
 
 
 KERNEL_SOURCES = ("segmented_gather_gemv_sgmv_amd/csrc/sgmv_api.hip",
+                  "segmented_gather_gemv_sgmv_amd/csrc/sgmv_mixed.hpp",
+                  "segmented_gather_gemv_sgmv_amd/csrc/sgmv_mfma.hpp",
                   "segmented_gather_gemv_sgmv_amd/csrc/sgmv_fused.hpp",
                   "segmented_gather_gemv_sgmv_amd/csrc/sgmv_gemv.hpp",
                   "segmented_gather_gemv_sgmv_amd/csrc/sgmv_device.hpp")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_lora_fused_kernel_llama7b_decode.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_lora_mixed_kernel_llama7b_decode.json")
 
 
 def kernel_source_hash() -> str:
@@ -655,7 +657,7 @@ def main(argv=None):
         "hbm_peak_frac": achieved / HBM_PEAK_GBPS,
         "roofline": {
             "bound": "hbm",
-            "kernel": ("lora_fused_kernel (one launch per step)"
+            "kernel": ("lora_mixed_kernel (one launch per step)"
                        if args.workload == "llama7b_decode" and args.row_ids is None and P == 1
                        and entry == "apply" else "every launch of one step"),
             "achieved": achieved,

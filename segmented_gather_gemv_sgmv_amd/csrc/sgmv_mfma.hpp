@@ -27,11 +27,13 @@
 // consecutive columns of one row (one 8-byte y access).  B^T is read from
 // an LDS copy of the B chunk with transposing LDS reads.  V is float32; to
 // feed it to a 16-bit MFMA without losing precision it is split as
-// v = hi + lo (both 16-bit)
-// and the K dimension is [hi | lo] against [B ; B], which keeps about 22
-// (fp16) or 16 (bf16) significant bits of v.  For fp16 the tile's v is first
-// scaled by a power of two so that max |v| lies in [2^12, 2^13) (exact,
-// undone on the result), keeping hi inside the fp16 range.
+// v = hi + mid + lo (each 16-bit, each the rounded remainder of the last)
+// and the K dimension is [hi | mid | lo | 0] against [B ; B ; B ; B],
+// padded to whole MFMA steps of 32.  Three bf16 terms hold 24 significant
+// bits, all of a float32 v; three fp16 terms hold more.  For fp16 the
+// tile's v is first scaled by a power of two so that max |v| lies in
+// [2^12, 2^13) (exact, undone on the result), keeping hi inside the fp16
+// range.
 #pragma once
 
 #include "sgmv_device.hpp"
@@ -124,6 +126,9 @@ struct MfmaShape {
     // different banks.
     static constexpr int kLdB = kCW + 16;
     static constexpr int kStageB = R * kLdB;  // LDS of the B chunk, in 16-bit units
+    // K of the expand's v operand: three 16-bit terms of each v, padded to
+    // whole MFMA steps of 32 (16-bit units per tile row of s_vh).
+    static constexpr int kVK = (3 * R + 31) / 32 * 32;
     static_assert(kStageB >= kT * kCW, "the y tile must fit over the B chunk");
     static_assert(kCW % 64 == 0, "the swizzle needs at least 16 groups per row");
     static_assert(kBV * kNT * 8 == R * kCW, "B chunk must split evenly over the threads");
@@ -256,9 +261,9 @@ __device__ __forceinline__ void expand_prefetch(ExpandRegs<R>& e,
 // Finishes an expand item once s_v (16 x R floats, rows >= nrows zero) is
 // complete and visible to the block: y[rows, c0 : c0 + kCW] += scale * V B.
 // The B chunk goes to LDS (s_b, kStageB 16-bit units), v is split into
-// 16-bit hi/lo halves (s_vh, range-scaled for fp16), Y^T = B^T V^T runs on
-// the MFMA units, and the results return through s_b so that y moves in
-// row-contiguous pieces.
+// three 16-bit terms (s_vh, 16 x kVK, range-scaled for fp16), Y^T = B^T V^T
+// runs on the MFMA units, and the results return through s_b so that y
+// moves in row-contiguous pieces.
 template <typename DT, int R>
 __device__ __forceinline__ void expand_apply(const ExpandRegs<R>& e, uint16_t* s_b,
                                              const float* s_v, uint16_t* s_vh, float* s_max,
@@ -296,14 +301,24 @@ __device__ __forceinline__ void expand_apply(const ExpandRegs<R>& e, uint16_t* s
             shift = min(max(13 - ex, -100), 100);
         }
     }
+    constexpr int VK = Sh::kVK;
     for (int t = tid; t < T * R; t += NT) {
         const int i = t / R;
         const int k = t - i * R;
         const float v = ldexpf(s_v[t], shift);
         const uint32_t hi = Ops::bits(v);
-        const uint32_t lo = Ops::bits(v - Ops::value(hi));
-        s_vh[i * 2 * R + k] = (uint16_t)hi;
-        s_vh[i * 2 * R + R + k] = (uint16_t)lo;
+        const float r1 = v - Ops::value(hi);
+        const uint32_t mid = Ops::bits(r1);
+        const uint32_t lo = Ops::bits(r1 - Ops::value(mid));
+        s_vh[i * VK + k] = (uint16_t)hi;
+        s_vh[i * VK + R + k] = (uint16_t)mid;
+        s_vh[i * VK + 2 * R + k] = (uint16_t)lo;
+    }
+    if constexpr (VK > 3 * R) {  // the padding of the K dimension meets zeros
+        for (int t = tid; t < T * (VK - 3 * R); t += NT) {
+            const int i = t / (VK - 3 * R);
+            s_vh[i * VK + 3 * R + (t - i * (VK - 3 * R))] = 0;
+        }
     }
     __syncthreads();
 
@@ -314,12 +329,12 @@ __device__ __forceinline__ void expand_apply(const ExpandRegs<R>& e, uint16_t* s
         const int cb = wid * CBW + q;
         acc[q] = mf32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 2 * R / 32; ++ks) {
-            // B rows kr .. kr + 7 (hi and lo both meet B row kr), columns
+        for (int ks = 0; ks < VK / 32; ++ks) {
+            // B rows kr .. kr + 7 (every term of v meets B row kr), columns
             // cb * 16 + [0, 16).
             const int kr = (ks * 32 + grp * 8) % R;
             const uint4 ab = lds_operand_tr(s_b + cb * 16, kr, Sh::kLdB, m);
-            const uint4 bv = *reinterpret_cast<const uint4*>(s_vh + m * 2 * R + ks * 32 + grp * 8);
+            const uint4 bv = *reinterpret_cast<const uint4*>(s_vh + m * VK + ks * 32 + grp * 8);
             acc[q] = Ops::mma(ab, bv, acc[q]);
         }
     }
@@ -389,7 +404,7 @@ __global__ __launch_bounds__(256) void lora_mfma_kernel(
                                                                        : Sh::kStageB];
     __shared__ float s_red[NW * 16 * R];
     __shared__ float s_v[T * R];
-    __shared__ __align__(16) uint16_t s_vh[T * 2 * R];      // per row: hi[0..R), lo[0..R)
+    __shared__ __align__(16) uint16_t s_vh[T * Sh::kVK];  // per row: hi, mid, lo terms of v
     __shared__ float s_max[NW];
     __shared__ int s_flag;
 
@@ -574,7 +589,7 @@ __global__ __launch_bounds__(256) void expand_mfma_kernel(
     __shared__ int s_scan[tile_scan_ints<NT>()];
     __shared__ __align__(16) uint16_t s_b[Sh::kStageB];  // B chunk, then the results
     __shared__ float s_v[T * R];
-    __shared__ __align__(16) uint16_t s_vh[T * 2 * R];
+    __shared__ __align__(16) uint16_t s_vh[T * Sh::kVK];
     __shared__ float s_max[NW];
 
     const int g = (int)(blockIdx.x / (unsigned)csplit);

@@ -322,8 +322,8 @@ struct MfmaTile {
         (Sh::kKcMax * R > Sh::kStageB ? Sh::kKcMax * R : Sh::kStageB) * 2;
     static_assert(Sh::kNW * 16 * R * 4 <= kRegion0, "the sums must fit over the A chunk");
     static constexpr int kOffV = kRegion0;                       // float [16 R]
-    static constexpr int kOffVh = kOffV + kT * R * 4;            // uint16 [16 2R]
-    static constexpr int kOffMax = kOffVh + kT * 2 * R * 2;      // float [NW]
+    static constexpr int kOffVh = kOffV + kT * R * 4;            // uint16 [16 kVK]
+    static constexpr int kOffMax = kOffVh + kT * Sh::kVK * 2;    // float [NW]
     static constexpr int kOffFlag = kOffMax + 16;                // int
     static constexpr int kLdsBytes = kOffFlag + 16;
 
