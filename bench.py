@@ -304,6 +304,8 @@ def run_linear(w, mode: str, steps: int, warmup: int, device="cuda:0"):
         if mode == "fused":
             sg.lora_linear(s["x"], s["W"], s["A"], s["B"], seg, ids, w.scale, bias=s["b"],
                            out=s["y"], workspace=ws)
+        elif mode == "base":
+            torch.addmm(s["b"], s["x"], s["W"].t(), out=s["y"])
         else:
             torch.addmm(s["b"], s["x"], s["W"].t(), out=s["y"])
             sg.lora_apply(s["y"], s["x"], s["A"], s["B"], seg, ids, w.scale, workspace=ws)
@@ -337,6 +339,33 @@ def run_linear(w, mode: str, steps: int, warmup: int, device="cuda:0"):
             "algorithmic_bytes": abytes, "achieved_hbm_GBps": abytes / us / 1e3,
             "hbm_peak_frac": abytes / us / 1e3 / HBM_PEAK_GBPS,
             "base_flops_TFLOPs": 2.0 * w.num_rows * w.H1 * w.H2 / us / 1e6}
+
+
+SWEEP_ROWS = (1, 2, 4, 8, 16, 32, 64, 128, 256)
+
+
+def rows_sweep(steps: int, warmup: int, rows=SWEEP_ROWS):
+    """Latency against batch size at the Llama-2-7B decode shape (4096 ->
+    4096, r = 16, fp16), the pages' microbenchmark: for each number of rows,
+    lora_apply with every row on its own adapter and with all rows on one
+    adapter, the base layer's own GEMM (torch's addmm, W [4096, 4096]), and
+    the base GEMM followed by the distinct-adapter add-on.  All cold (inputs
+    rotated over >= 1 GiB), each a HIP graph of `steps` steps timed with HIP
+    events.  Yields one dict per row count."""
+    import workloads as wl
+    for R in rows:
+        out = {"rows": R}
+        for tag, distinct in (("distinct", True), ("same", False)):
+            w = wl.decode_batch(R, distinct=distinct)
+            res = run_gpu(w, steps, warmup, replays=3)
+            us = res["gpu_ms"] * 1e3 / steps
+            out[f"sgmv_{tag}_us"] = us
+            out[f"sgmv_{tag}_GBps"] = algorithmic_bytes(w) / us / 1e3
+            out[f"sgmv_{tag}_fallback_flag"] = res["fallback_flag"]
+        w = wl.decode_batch(R, distinct=True)
+        out["base_gemm_us"] = run_linear(w, "base", steps, warmup)["us_per_call"]
+        out["base_plus_sgmv_us"] = run_linear(w, "unfused", steps, warmup)["us_per_call"]
+        yield out
 
 
 def copy_floor(w, steps: int, warmup: int, device="cuda:0", nbytes=None):
@@ -565,7 +594,10 @@ def main(argv=None):
     ap.add_argument("--projections", type=int, default=1, choices=range(1, 9), metavar="P",
                     help="P add-ons of the workload's shape over the same batch in one "
                          "lora_apply_multi call (e.g. a layer's q/k/v/o projections)")
-    ap.add_argument("--linear", choices=("fused", "unfused"), default=None,
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead: latency against rows per call (1..256) at the decode shape, "
+                         "distinct and identical adapters, beside the base layer's GEMM")
+    ap.add_argument("--linear", choices=("fused", "unfused", "base"), default=None,
                     help="instead: time the adapted linear layer over the workload's batch, "
                          "base product fused in (lora_linear) or not (addmm + lora_apply)")
     ap.add_argument("--entry", choices=("apply", "shrink", "expand"), default="apply",
@@ -603,6 +635,10 @@ def main(argv=None):
         return 0
     if args.linear:
         print(json.dumps(run_linear(w, args.linear, args.steps, args.warmup)), flush=True)
+        return 0
+    if args.sweep:
+        for point in rows_sweep(min(args.steps, 400), min(args.warmup, 40)):
+            print(json.dumps(point), flush=True)
         return 0
     P = args.projections
     entry = args.entry

@@ -25,7 +25,9 @@ import os
 import threading
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIBRARY = os.path.join(_HERE, "libsgmv.so")
+# SGMV_LIBRARY names another build of the same library (e.g. the host-side
+# AddressSanitizer build that the CPU tests load); by default the in-tree one.
+LIBRARY = os.environ.get("SGMV_LIBRARY") or os.path.join(_HERE, "libsgmv.so")
 
 SGMV_F32, SGMV_F16, SGMV_BF16 = 0, 1, 2
 SGMV_MAX_RANK = 128

@@ -349,27 +349,46 @@ long long mixed_bound(long long R, long long S, const MixedShape& ms, const long
     return (long long)best + 1;
 }
 
-// Chunk sizes for a target of `tb` bytes per shrink item: an item of a
-// tall tile reads its rows of A and, for each of its T rows, the same
+// Chunk sizes of class c for a target of `tb` bytes per shrink item: an item
+// of a tall tile reads its rows of A and, for each of its T rows, the same
 // stretch of x; a one-row item reads its rows of A (its stretch of x, 1/r
 // of that, stays out of the count so that power-of-two targets give
 // power-of-two chunks).  One-launch long chunks stay within one LDS chunk
 // of A; two-launch ones may span several (summed in order).
-MixedSplit mixed_split(const MixedShape& ms, long long tb, int H1, int H2, bool one_launch) {
+void mixed_split_class(const MixedShape& ms, int c, long long tb, int H1, int H2,
+                       bool one_launch, MixedSplit& sp) {
+    const int unit = ms.unit[c];
+    const long long per_row = (long long)(ms.r + (ms.T[c] > 1 ? ms.T[c] : 0)) * ms.e;
+    long long hh = tb / per_row / unit * unit;
+    if (hh < unit) hh = unit;
+    if (ms.hmax[c] > 0 && one_launch && hh > ms.hmax[c]) hh = ms.hmax[c];
+    const long long hcap = ((long long)H1 + unit - 1) / unit * unit;
+    if (hh > hcap) hh = hcap;
+    const long long kk = (H1 + hh - 1) / hh;
+    hh = ((H1 + kk - 1) / kk + unit - 1) / unit * unit;
+    sp.k[c] = (int)kk;
+    sp.h[c] = (int)hh;
+    sp.c[c] = (H2 + ms.cw[c] - 1) / ms.cw[c];
+}
+
+// Each class's split on its own: the finest byte target whose items, were
+// the whole batch of that class (its own worst case), fit `budget` -- with
+// at most `max_k` chunks -- or the coarsest target if none does.  `expand`
+// counts expand items as well as shrink items.
+MixedSplit mixed_split(const MixedShape& ms, int R, int S, int H1, int H2, bool one_launch,
+                       long long budget, int max_k) {
+    static const long long kTargets[] = {4096, 8192, 16384, 32768, 65536, 131072, 262144};
+    const int n_targets = one_launch ? 5 : 7;
     MixedSplit sp{};
     for (int c = 0; c < 3; ++c) {
-        const int unit = ms.unit[c];
-        const long long per_row = (long long)(ms.r + (ms.T[c] > 1 ? ms.T[c] : 0)) * ms.e;
-        long long hh = tb / per_row / unit * unit;
-        if (hh < unit) hh = unit;
-        if (ms.hmax[c] > 0 && one_launch && hh > ms.hmax[c]) hh = ms.hmax[c];
-        const long long hcap = ((long long)H1 + unit - 1) / unit * unit;
-        if (hh > hcap) hh = hcap;
-        const long long kk = (H1 + hh - 1) / hh;
-        hh = ((H1 + kk - 1) / kk + unit - 1) / unit * unit;
-        sp.k[c] = (int)kk;
-        sp.h[c] = (int)hh;
-        sp.c[c] = (H2 + ms.cw[c] - 1) / ms.cw[c];
+        long long unit_q[3] = {0, 0, 0};
+        unit_q[c] = 1;
+        const long long tiles_c = mixed_bound(R, S, ms, unit_q);
+        for (int i = 0; i < n_targets; ++i) {
+            mixed_split_class(ms, c, kTargets[i], H1, H2, one_launch, sp);
+            const long long per_tile = sp.k[c] + (one_launch ? sp.c[c] : 0);
+            if (tiles_c * per_tile <= budget && sp.k[c] <= max_k) break;
+        }
     }
     return sp;
 }
@@ -383,36 +402,24 @@ struct MixedPlan {
     int kmax;              // partial chunks the workspace holds (either form)
 };
 
-// Pure function of the shapes: the one-launch form with the finest chunks
-// (at most kMixedMaxSplit per tile) whose items fit one resident round --
-// the coarsest if none do -- unless even that needs more than two rounds or
-// more tiles than there are counters; then the two-launch form, whose
-// shrink launch takes the finest chunks that fit two rounds.
+// Pure function of the shapes: each class split on its own (mixed_split),
+// one launch when even the worst mix of classes needs at most two resident
+// rounds of items and the tiles fit the counters, else two launches, whose
+// shrink launch splits each class to fit two rounds of workgroups.
 MixedPlan make_mixed_plan(const MixedShape& ms, int R, int S, int H1, int H2) {
     MixedPlan p{};
     if (!ms.ok || S < 1 || R < 1 || S > kMixedMaxSegments) return p;
     const long long ones[3] = {1, 1, 1};
     p.tiles = mixed_bound(R, S, ms, ones);
-    static const long long kTargets[] = {4096, 8192, 16384, 32768, 65536, 131072, 262144};
-    bool found = false;
-    for (int i = 0; i < 5 && !found; ++i) {
-        p.one = mixed_split(ms, kTargets[i], H1, H2, true);
-        const long long q[3] = {p.one.k[0] + p.one.c[0], p.one.k[1] + p.one.c[1],
-                                p.one.k[2] + p.one.c[2]};
-        p.grid_one = mixed_bound(R, S, ms, q);
-        int kmx = 0;
-        for (int c = 0; c < 3; ++c) kmx = std::max(kmx, p.one.k[c]);
-        found = p.grid_one <= kMixedBudget && kmx <= kMixedMaxSplit;
-    }
+    p.one = mixed_split(ms, R, S, H1, H2, true, kMixedBudget, kMixedMaxSplit);
+    const long long q[3] = {p.one.k[0] + p.one.c[0], p.one.k[1] + p.one.c[1],
+                            p.one.k[2] + p.one.c[2]};
+    p.grid_one = mixed_bound(R, S, ms, q);
     p.two = p.grid_one > 2 * kMixedBudget || p.tiles > kCounterSlots;
-    found = false;
-    for (int i = 0; i < 7 && !found; ++i) {
-        p.two_sp = mixed_split(ms, kTargets[i], H1, H2, false);
-        const long long qk[3] = {p.two_sp.k[0], p.two_sp.k[1], p.two_sp.k[2]};
-        p.grid_shrink = mixed_bound(R, S, ms, qk);
-        found = p.grid_shrink <= 2 * kMixedBudget;
-    }
+    p.two_sp = mixed_split(ms, R, S, H1, H2, false, 2 * kMixedBudget, 1 << 15);
+    const long long qk[3] = {p.two_sp.k[0], p.two_sp.k[1], p.two_sp.k[2]};
     const long long qc[3] = {p.two_sp.c[0], p.two_sp.c[1], p.two_sp.c[2]};
+    p.grid_shrink = mixed_bound(R, S, ms, qk);
     p.grid_expand = mixed_bound(R, S, ms, qc);
     p.kmax = 0;
     bool fits = true;

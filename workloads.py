@@ -203,6 +203,21 @@ def mixed_batch(seed=0, long_rows=(512, 512), short=128, H=4096, r=16, dtype="f1
     return make_workload(name, dtype, H, H, r, num_adapters, lengths, ids, 32.0 / r, rng=rng)
 
 
+def decode_batch(rows: int, distinct: bool = True, seed=0, H=4096, r=16, dtype="f16",
+                 num_adapters=256) -> Workload:
+    """A decode batch of ``rows`` rows at the Llama-2-7B projection shape:
+    every row its own one-row segment on its own adapter (``distinct``,
+    adapters 0..rows-1), or all rows one segment on adapter 0 -- the two
+    ends of the pages' comparison of distinct and identical models in a
+    batch.  fp16, s = 2."""
+    if distinct:
+        lengths, ids = [1] * rows, list(range(rows))
+    else:
+        lengths, ids = [rows], [0]
+    name = f"decode_{'distinct' if distinct else 'same'}_{H}_r{r}_{rows}rows"
+    return make_workload(name, dtype, H, H, r, num_adapters, lengths, ids, 32.0 / r, seed=seed)
+
+
 CONFIGS = {
     0: tiny,
     1: llama7b_decode,
