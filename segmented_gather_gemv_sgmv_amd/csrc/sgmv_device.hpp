@@ -110,6 +110,23 @@ __device__ __forceinline__ void store16(void* p, const uint4& v) {
     *reinterpret_cast<uint4*>(p) = v;
 }
 
+// The same accesses with the nontemporal hint, for y: an expand reads each
+// piece of y once and writes it back once, so nothing the caches keep of
+// it is used again within the call.  On gfx950 a read-modify-write stream
+// that carries the hint on both the load and the store runs markedly
+// closer to the HBM rate than one without (measured: 32-row x 1 KB tiles
+// of a 4096 x 4096 fp16 matrix, 12.1 us against 17.7 us); 8-byte pieces
+// do not gain, and read-only streams (x, the weights) do not either.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load16_stream(const void* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store16_stream(void* p, const uint4& v) {
+    const u32x4_t w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
+}
+
 // ---------------------------------------------------------------------------
 // Scans.
 // ---------------------------------------------------------------------------

@@ -222,6 +222,108 @@ __device__ __forceinline__ void shrink_chunk_mfma(const typename DT::storage* __
     __syncthreads();  // s_a and s_red free again
 }
 
+// The shrink of [h_lo, h_hi) (multiples of 8, longer than one LDS chunk)
+// for a tile of nrows <= 16 rows.  A chain of shrink_chunk_mfma calls
+// would wait for each chunk's x before requesting the next; here the x
+// operand of a whole stretch of chunks (8 K steps of 32 per wave, 4 at
+// r >= 64, where the A chunks and accumulators need the registers) is
+// requested before any of it is used, the next chunk of A is requested
+// while the current one is multiplied, and each wave's products stay in
+// its MFMA accumulators across chunks (in chunk order).  The four waves'
+// sums are added in wave order at the end; emit(i, k, value) is called
+// once per (i < nrows, k < R) from threads tid < 16 * R.  Begins and ends
+// with the block synchronised; s_red may overlap s_a.
+template <typename DT, int R, int KC, typename Emit>
+__device__ __forceinline__ void shrink_long_mfma(const typename DT::storage* __restrict__ A,
+                                                 const typename DT::storage* __restrict__ xr,
+                                                 int nrows, int H1, int h_lo, int h_hi,
+                                                 uint16_t* s_a, float* s_red, Emit&& emit) {
+    using Sh = MfmaShape<R, KC>;
+    using Ops = MfmaOps<DT>;
+    constexpr int NB = R / 16;
+    constexpr int XS = Sh::kXSteps;            // K steps of 32 per wave and chunk
+    constexpr int kStretch = R >= 64 ? 4 : 8;  // K steps of x per wave requested together
+    constexpr int CPS = XS >= kStretch ? 1 : kStretch / XS;  // chunks per stretch
+    constexpr int KQ = KC / Sh::kNW;           // h of a chunk per wave
+    constexpr int kAV = KC * R / 8 / Sh::kNT;  // 16-byte pieces of an A chunk per thread
+    static_assert(kAV * Sh::kNT * 8 == KC * R, "A chunk must split evenly");
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wid = tid / kWave;
+    const int m = lane & 15;
+    const int grp = lane >> 4;
+    const bool row_ok = m < nrows;
+    const typename DT::storage* xm = xr + (long long)m * H1;
+
+    mf32x4 acc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = mf32x4{0.f, 0.f, 0.f, 0.f};
+    uint4 av[kAV];
+    auto load_a = [&](int c_lo) {
+        const int n16 = min(KC, h_hi - c_lo) * R / 8;
+        const typename DT::storage* Ac = A + (long long)c_lo * R;
+#pragma unroll
+        for (int u = 0; u < kAV; ++u) {
+            const int t = tid + u * Sh::kNT;
+            av[u] = t < n16 ? load16(Ac + (long long)t * 8) : make_uint4(0, 0, 0, 0);
+        }
+    };
+    load_a(h_lo);
+    for (int s_lo = h_lo; s_lo < h_hi; s_lo += CPS * KC) {
+        uint4 xa[CPS][XS];
+#pragma unroll
+        for (int j = 0; j < CPS; ++j)
+#pragma unroll
+            for (int s = 0; s < XS; ++s) {
+                const int h = s_lo + j * KC + wid * KQ + s * 32 + grp * 8;
+                xa[j][s] = (h < h_hi && row_ok) ? load16(xm + h) : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+        for (int j = 0; j < CPS; ++j) {
+            const int c_lo = s_lo + j * KC;
+            if (c_lo < h_hi) {  // block-uniform
+                const int kc = min(KC, h_hi - c_lo);
+                __syncthreads();  // every wave is done with the previous chunk
+#pragma unroll
+                for (int u = 0; u < kAV; ++u) {
+                    const int t = tid + u * Sh::kNT;
+                    if (t < kc * R / 8) store16(s_a + t * 8, av[u]);
+                }
+                if (c_lo + KC < h_hi) load_a(c_lo + KC);
+                __syncthreads();
+#pragma unroll
+                for (int s = 0; s < XS; ++s) {
+                    // Rows hl .. hl + 7 of the chunk are all inside it or
+                    // all past it; past it, LDS holds no data of this chunk.
+                    const int hl = wid * KQ + s * 32 + grp * 8;
+                    const bool in = hl < kc;
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        uint4 hb = lds_operand_tr(s_a + nb * 16, hl, R, m);
+                        if (!in) hb = make_uint4(0, 0, 0, 0);
+                        acc[nb] = Ops::mma(xa[j][s], hb, acc[nb]);
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();  // s_red lies over s_a
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s_red[(wid * 16 + 4 * grp + i) * R + nb * 16 + m] = acc[nb][i];
+    __syncthreads();
+    for (int t = tid; t < 16 * R; t += Sh::kNT) {
+        const int i = t / R;
+        const int k = t - i * R;
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < Sh::kNW; ++w) sum += s_red[(w * 16 + i) * R + k];
+        if (i < nrows) emit(i, k, sum);
+    }
+    __syncthreads();  // s_a and s_red free again
+}
+
 // The part of an expand item (tile rows x columns [c0, c0 + kCW)) that does
 // not depend on v, loaded first: this thread's 16-byte pieces of the B chunk
 // and the y values its lane updates.
@@ -253,7 +355,7 @@ __device__ __forceinline__ void expand_prefetch(ExpandRegs<R>& e,
         const int row = u / (CW / 8);
         const int col = c0 + (u % (CW / 8)) * 8;
         e.yv[j] = (u < 2 * CW && row < nrows && col < H2)
-                      ? load16(yr + (long long)row * H2 + col)
+                      ? load16_stream(yr + (long long)row * H2 + col)
                       : make_uint4(0, 0, 0, 0);
     }
 }
@@ -377,7 +479,8 @@ __device__ __forceinline__ void expand_apply(const ExpandRegs<R>& e, uint16_t* s
         if (u < 2 * CW && row < nrows && c0 + g * 4 < H2) {
             const uint2 a0 = s_y[row * G + (g ^ row)];
             const uint2 a1 = s_y[row * G + ((g + 1) ^ row)];
-            store16(yr + (long long)row * H2 + c0 + g * 4, make_uint4(a0.x, a0.y, a1.x, a1.y));
+            store16_stream(yr + (long long)row * H2 + c0 + g * 4,
+                           make_uint4(a0.x, a0.y, a1.x, a1.y));
         }
     }
 }

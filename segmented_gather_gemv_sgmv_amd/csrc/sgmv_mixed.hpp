@@ -186,7 +186,7 @@ struct VecTile {
                 DT::unpack(yv[i], yf);
 #pragma unroll
                 for (int q = 0; q < kVec; ++q) yf[q] = fmaf(scale, acc[i][q], yf[q]);
-                store16(y + (long long)(t.row0 + i) * H2 + j, DT::pack(yf));
+                store16_stream(y + (long long)(t.row0 + i) * H2 + j, DT::pack(yf));
             }
         }
     }
@@ -200,8 +200,9 @@ struct VecTile {
             bv[kk] = active ? load16(Bj + (long long)kk * H2) : make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < RB; ++i)
-            yv[i] = (active && i < t.nrows) ? load16(y + (long long)(t.row0 + i) * H2 + j)
-                                            : make_uint4(0, 0, 0, 0);
+            yv[i] = (active && i < t.nrows)
+                        ? load16_stream(y + (long long)(t.row0 + i) * H2 + j)
+                        : make_uint4(0, 0, 0, 0);
     }
 
     // One-launch expand item: loads that do not need v go out first, then
@@ -343,36 +344,32 @@ struct MfmaTile {
         return reinterpret_cast<float*>(lds + kOffMax);
     }
 
-    // The shrink of [h_lo, h_hi) for the tile; ranges longer than one LDS
-    // chunk are summed chunk by chunk, in order, into `acc` (16 R floats of
-    // LDS that the caller does not need meanwhile) before emit() sees them.
+    // The shrink of [h_lo, h_hi) for the tile, any length (ranges longer
+    // than one LDS chunk of A stream through shrink_long_mfma).
     template <typename Emit>
     __device__ static __forceinline__ void shrink_range(const Tile& t, const st* __restrict__ x,
                                                         const st* __restrict__ A_stack, int H1,
                                                         int h_lo, int h_hi, unsigned char* lds,
-                                                        float* acc, Emit&& emit) {
+                                                        Emit&& emit) {
         const st* A = A_stack + (long long)t.adapter * H1 * R;
         const st* xr = x + (long long)t.row0 * H1;
-        if (h_hi - h_lo <= Sh::kKcMax) {
+        if (h_hi - h_lo <= Sh::kKcMax)
             shrink_chunk_mfma<DT, R, true, KC>(A, xr, t.nrows, H1, h_lo, h_hi, s_a(lds),
                                                s_red(lds), emit);
-            return;
-        }
-        for (int c_lo = h_lo; c_lo < h_hi; c_lo += Sh::kKcMax) {
-            const bool first = c_lo == h_lo;
-            shrink_chunk_mfma<DT, R, true, KC>(A, xr, t.nrows, H1, c_lo,
-                                               min(h_hi, c_lo + Sh::kKcMax),
-                                           s_a(lds), s_red(lds), [&](int i, int k, float v) {
-                                               float* a = &acc[i * R + k];
-                                               *a = first ? v : *a + v;
-                                           });
-        }
-        // Each value was written by the thread that emits it (same loop).
-        for (int e = threadIdx.x; e < kT * R; e += NT) {
-            const int i = e / R;
-            if (i < t.nrows) emit(i, e - i * R, acc[e]);
-        }
-        __syncthreads();
+        else
+            shrink_long_mfma<DT, R, (KC >= 256 ? KC / 2 : KC)>(A, xr, t.nrows, H1, h_lo, h_hi,
+                                                               s_a(lds), s_red(lds), emit);
+    }
+
+    // One-launch ranges are single LDS chunks (the plan keeps them so).
+    template <typename Emit>
+    __device__ static __forceinline__ void shrink_chunk(const Tile& t, const st* __restrict__ x,
+                                                        const st* __restrict__ A_stack, int H1,
+                                                        int h_lo, int h_hi, unsigned char* lds,
+                                                        Emit&& emit) {
+        shrink_chunk_mfma<DT, R, true, KC>(A_stack + (long long)t.adapter * H1 * R,
+                                           x + (long long)t.row0 * H1, t.nrows, H1, h_lo, h_hi,
+                                           s_a(lds), s_red(lds), emit);
     }
 
     __device__ static __forceinline__ void shrink_item(const Tile& t, int p, int hps,
@@ -383,7 +380,7 @@ struct MfmaTile {
         const int h_lo = p * hps;
         const int h_hi = min(H1, h_lo + hps);
         float* out = partials + (long long)p * row_stride + (long long)t.row0 * R;
-        shrink_range(t, x, A_stack, H1, h_lo, h_hi, lds, s_v(lds),
+        shrink_chunk(t, x, A_stack, H1, h_lo, h_hi, lds,
                      [&](int i, int k, float v) { store_partial(&out[i * R + k], v); });
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_waitcnt(0);
@@ -419,12 +416,10 @@ struct MfmaTile {
             if (tid == 0) __hip_atomic_store(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             for (int e = tid; e < kT * R; e += NT) sv[e] = 0.f;
             __syncthreads();
-            // One-launch ranges are single LDS chunks (the plan keeps them
-            // so), so no accumulator beyond s_v is needed.
             for (int pp = 0; pp < ksplit; ++pp) {
                 const int h_lo = pp * hps;
                 const int h_hi = min(H1, h_lo + hps);
-                shrink_range(t, x, A_stack, H1, h_lo, h_hi, lds, nullptr,
+                shrink_chunk(t, x, A_stack, H1, h_lo, h_hi, lds,
                              [&](int i, int k, float v) { sv[i * R + k] += v; });
             }
             expand_prefetch<DT, R>(er, B, yr, t.nrows, H2, c0);
@@ -445,7 +440,7 @@ struct MfmaTile {
         const int h_lo = p * hps;
         const int h_hi = min(H1, h_lo + hps);
         float* out = partials + (long long)p * row_stride + (long long)t.row0 * R;
-        shrink_range(t, x, A_stack, H1, h_lo, h_hi, lds, s_v(lds), [&](int i, int k, float v) {
+        shrink_range(t, x, A_stack, H1, h_lo, h_hi, lds, [&](int i, int k, float v) {
             if (v_final) store_partial(&out[i * R + k], v);
             else out[i * R + k] = v;
         });
@@ -750,7 +745,7 @@ __global__ __launch_bounds__(kMixedThreads, 4) void lora_mixed_kernel(
 // items.  With v_final (sgmv_shrink), each tile's last item reduces the
 // partials into v (tile counters: long tiles, then short, then single).
 template <typename DT, int R, typename LP, typename SP, typename GP>
-__global__ __launch_bounds__(kMixedThreads) void shrink_mixed_kernel(
+__global__ __launch_bounds__(kMixedThreads, R <= 32 ? 6 : (R == 64 ? 5 : 1)) void shrink_mixed_kernel(
     const typename DT::storage* __restrict__ x, const typename DT::storage* __restrict__ A_stack,
     const int* __restrict__ seg_indptr, const int* __restrict__ adapter_ids, int S, int num_rows,
     int num_adapters, int H1, float* __restrict__ partials, MixedSplit sp,
