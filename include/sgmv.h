@@ -252,8 +252,14 @@ int lora_apply_multi(const sgmv_lora_problem* problems, int32_t num_problems,
  * fp16/bf16 with H1 and H2 multiples of 8 and 16-byte aligned x, W, y,
  * bias and B_stack run on the matrix cores; any other call (float32
  * included) takes a slow element-wise kernel with the same definition.
- * The call enqueues two launches: the shrink of the add-on (skipped when
- * num_segments == 0), then the fused layer.
+ * Decode batches on the matrix cores (at most 64 rows, r in {16, 32, 64,
+ * 128}, 16-byte aligned A_stack) take one launch: each workgroup of the
+ * layer also computes a share of x @ A_a, publishes it, and waits for the
+ * others' before adding its correction (the single-launch hand-off of
+ * lora_apply, with the same patience, sgmv_set_fused_wait(); a workgroup
+ * that stops waiting recomputes its share with the same arithmetic, so
+ * the bits do not depend on it).  Other calls enqueue two launches: the
+ * shrink of the add-on (skipped when num_segments == 0), then the layer.
  *
  * workspace: at least lora_linear_workspace_bytes(...) bytes, with the
  * conventions of "Workspace" above.  Returns as lora_apply; num_rows == 0
@@ -291,7 +297,8 @@ int sgmv_load_adapter(void* A_stack, void* B_stack, int32_t slot, int32_t count,
 /*
  * Process-wide patience, in seconds (0 <= seconds <= 10; default 0.02), of
  * the single-kernel lora_apply's expand workgroups waiting for their shrink
- * workgroups.  A workgroup that stops waiting computes its input itself with
+ * workgroups (and of the one-launch lora_linear's workgroups waiting for
+ * each other's shares of x @ A_a).  A workgroup that stops waiting computes its input itself with
  * the same arithmetic in the same order, so results never depend on this
  * setting; 0 makes every expand workgroup do so without waiting (that is
  * how the path is tested).  This is the library's only state.  Returns SGMV_OK or

@@ -12,6 +12,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <tuple>
 #include <type_traits>
@@ -740,7 +741,9 @@ LinearPlan make_linear_plan(int M, int S, int H1, int H2, int r, int dtype) {
 }
 
 size_t linear_v_bytes(const LinearPlan& lp, int M, int r) {
-    return round256((size_t)lp.shrink.ksplit * (size_t)M * (size_t)r * sizeof(float));
+    // the shrink launch's chunk partials, or (folded) one per K range
+    const size_t planes = (size_t)std::max<long long>(lp.shrink.ksplit, lp.ksplit);
+    return round256(planes * (size_t)M * (size_t)r * sizeof(float));
 }
 
 size_t linear_part_bytes(const LinearPlan& lp) {
@@ -748,18 +751,34 @@ size_t linear_part_bytes(const LinearPlan& lp) {
     return (size_t)lp.tiles * (size_t)lp.ksplit * (size_t)lp.BM * (size_t)lp.BN * sizeof(float);
 }
 
-template <typename DT, typename SH>
+template <typename DT, typename SH, bool kFold = false>
 void launch_linear_tiled(void* y, const void* x, const void* W, const void* bias, const void* B,
                          const float* vpart, long long vstride, int vsplit, const int32_t* seg,
                          const int32_t* ids, int S, int M, int nad, int H1, int H2, int r,
                          float scale, float* part, int* counters, const LinearPlan& lp,
-                         hipStream_t st) {
+                         hipStream_t st, const void* A = nullptr, long long wait = -1) {
     using T = typename DT::storage;
-    const unsigned grid = (unsigned)(lp.tiles * lp.ksplit);
-    launch(&linear_lora_kernel<DT, SH>, dim3(grid), dim3(kLinThreads), st, (T*)y, (const T*)x,
-           (const T*)W, (const T*)bias, (const T*)B, vpart, vstride, vsplit, seg, ids, S, M, nad,
-           H1, H2, r, scale, part, counters, kCounterStride, lp.ksplit, lp.cps, (int)lp.tiles_n,
-           (int)lp.tiles);
+    // folded: one shrink workgroup per row and K range ahead of the tiles
+    const int n_shrink = kFold ? M * (int)lp.ksplit : 0;
+    const unsigned grid = (unsigned)(n_shrink + lp.tiles * lp.ksplit);
+    launch(&linear_lora_kernel<DT, SH, kFold>, dim3(grid), dim3(kLinThreads), st, (T*)y,
+           (const T*)x, (const T*)W, (const T*)bias, (const T*)B, vpart, vstride, vsplit, seg, ids,
+           S, M, nad, H1, H2, r, scale, part, counters, kCounterStride, lp.ksplit, lp.cps,
+           (int)lp.tiles_n, (int)lp.tiles, (const T*)A,
+           kFold ? counters + lp.tiles * kCounterStride : (int*)nullptr,
+           kFold ? counters + kCounterInts - 1 : (int*)nullptr, wait, n_shrink);
+}
+
+// Whether lora_linear folds its shrink into the tile launch: decode tiles
+// (one row block), an MFMA rank, a rank share that the correction takes in
+// one pass, room for the extra counter, and counts that fit its halves
+// (shrink workgroups in the low 16 bits, tile workgroups in the rest).
+bool linear_folds(const LinearPlan& lp, int M, int S, int r, int dtype) {
+    if (lp.cfg != 0 || S < 1 || dtype == SGMV_F32) return false;
+    if (r != 16 && r != 32 && r != 64 && r != 128) return false;
+    if ((r + lp.ksplit - 1) / lp.ksplit > kLinRG) return false;
+    if (lp.tiles + 1 > kCounterSlots) return false;
+    return (long long)M * lp.ksplit < (1 << 16) && lp.tiles * lp.ksplit < (1 << 15);
 }
 
 // -- scratch of lora_apply_noalloc ------------------------------------------
@@ -1431,8 +1450,16 @@ int lora_linear(void* y, const void* x, const void* W, const void* bias, const v
     float* vpart = (float*)((char*)workspace + kCounterBytes);
     float* part = (float*)((char*)vpart + linear_v_bytes(lp, num_rows, r));
     const long long vstride = (long long)num_rows * r;
-    const int vsplit = lp.shrink.ksplit;
-    if (num_segments > 0) {
+    const bool tiled = lp.cfg >= 0 && aligned16(x) && aligned16(W) && aligned16(y) &&
+                       aligned16(B_stack) && aligned16(bias);
+    // Decode tiles fold the shrink into their own launch (linear_lora_kernel).
+    const bool fold =
+        tiled && aligned16(A_stack) && linear_folds(lp, num_rows, num_segments, r, dtype);
+    const int vsplit = fold ? lp.ksplit : lp.shrink.ksplit;
+    const double wait_s = fused_wait_seconds();
+    const long long wait =
+        wait_s < 1e-300 ? -1 : (long long)(wait_s * (double)wall_ticks_per_second());
+    if (num_segments > 0 && !fold) {
         with_dtype(dtype, [&](auto dt) {
             using DT = decltype(dt);
             dispatch_shrink<DT>(vpart, vstride, x, A_stack, seg_indptr, adapter_ids, num_segments,
@@ -1440,12 +1467,17 @@ int lora_linear(void* y, const void* x, const void* W, const void* bias, const v
         });
         if ((rc = launch_status()) != SGMV_OK) return rc;
     }
-    const bool tiled = lp.cfg >= 0 && aligned16(x) && aligned16(W) && aligned16(y) &&
-                       aligned16(B_stack) && aligned16(bias);
     with_dtype(dtype, [&](auto dt) {
         using DT = decltype(dt);
         using T = typename DT::storage;
         if constexpr (!std::is_same<DT, F32>::value) {
+            if (fold) {
+                launch_linear_tiled<DT, LinSkinny, true>(
+                    y, x, W, bias, B_stack, vpart, vstride, vsplit, seg_indptr, adapter_ids,
+                    num_segments, num_rows, num_adapters, H1, H2, r, scale, part, counters, lp,
+                    st, A_stack, wait);
+                return;
+            }
             if (tiled) {
                 if (lp.cfg == 0)
                     launch_linear_tiled<DT, LinSkinny>(y, x, W, bias, B_stack, vpart, vstride,

@@ -107,6 +107,27 @@ __device__ __forceinline__ void linear_rank_share(int r, int ksplit, int q, int&
     k_hi = k_lo + rs < r ? k_lo + rs : r;
 }
 
+// The first pass of v for this workgroup's share of the ranks (its first
+// kLinRG ranks), summed over the shrink's chunks in order, for every tile
+// row below M.
+template <bool kCoherent>
+__device__ __forceinline__ void linear_prepare_v(float* s_v, const float* __restrict__ vpart,
+                                                 long long vstride, int vsplit, int M, int r,
+                                                 int ksplit, int q, int m0, int BM) {
+    int k_lo, k_hi;
+    linear_rank_share(r, ksplit, q, k_lo, k_hi);
+    const int gn = k_hi - k_lo < kLinRG ? k_hi - k_lo : kLinRG;
+    for (int e = threadIdx.x; e < BM * gn; e += kLinThreads) {
+        const int il = e / gn, kk = e - il * gn;
+        const float* p = vpart + (long long)(m0 + il) * r + k_lo + kk;
+        float v = 0.f;
+        if (m0 + il < M)
+            v = kCoherent ? sum_partials_coherent(const_cast<float*>(p), vstride, vsplit)
+                          : sum_partials(p, vstride, vsplit);
+        s_v[il * kLinRG + kk] = v;
+    }
+}
+
 // What the correction needs that does not depend on the base product, done
 // before the main loop so that its round trips overlap the first chunks'
 // loads: each tile row's adapter (s_aid) and the first pass of v (the
@@ -114,6 +135,10 @@ __device__ __forceinline__ void linear_rank_share(int r, int ksplit, int q, int&
 // order).  v is summed for every row below M; rows without an adapter
 // never use theirs.  The caller must make s_seg / s_ids visible first and
 // synchronise before s_aid / s_v are read.
+// With kCoherent, v's partials are read with agent-scope loads: they were
+// published during this launch (the folded shrink) rather than by an
+// earlier one.  kWithV = false leaves s_v to the caller.
+template <bool kCoherent = false, bool kWithV = true>
 __device__ __forceinline__ void linear_prepare(int* s_aid, float* s_v, const int* s_seg,
                                                const int* s_ids, bool seg_lds,
                                                const float* __restrict__ vpart, long long vstride,
@@ -129,15 +154,8 @@ __device__ __forceinline__ void linear_prepare(int* s_aid, float* s_v, const int
                         : row_adapter(seg_indptr, adapter_ids, S, m0 + i, num_adapters);
         s_aid[i] = a;
     }
-    int k_lo, k_hi;
-    linear_rank_share(r, ksplit, q, k_lo, k_hi);
-    const int gn = k_hi - k_lo < kLinRG ? k_hi - k_lo : kLinRG;
-    for (int e = tid; e < BM * gn; e += kLinThreads) {
-        const int il = e / gn, kk = e - il * gn;
-        s_v[il * kLinRG + kk] =
-            m0 + il < M ? sum_partials(vpart + (long long)(m0 + il) * r + k_lo + kk, vstride, vsplit)
-                        : 0.f;
-    }
+    if constexpr (kWithV)
+        linear_prepare_v<kCoherent>(s_v, vpart, vstride, vsplit, M, r, ksplit, q, m0, BM);
 }
 
 // The part of an adapted-linear tile that follows the base product, shared
@@ -147,7 +165,35 @@ __device__ __forceinline__ void linear_prepare(int* s_aid, float* s_v, const int
 // share of the ranks of scale * v B_a, combines the K ranges (the last
 // workgroup of a tile to arrive sums them in a fixed order), adds the bias,
 // rounds once and stores y.
-template <typename DT, int BM, int BN, int TP>
+// The B rows of the correction's first four ranks for this thread's
+// epilogue pieces, as linear_finish reads them: loads that do not depend on
+// v or on the base product, so a caller can issue them before waiting for
+// either.
+template <typename DT, int BM, int BN>
+__device__ __forceinline__ void linear_prefetch_b(uint4 (&pre)[BM * BN / 8 / kLinThreads][4],
+                                                  const int* s_aid,
+                                                  const typename DT::storage* __restrict__ B_stack,
+                                                  int H2, int r, int ksplit, int q, int n0) {
+    constexpr int kPieces = BM * BN / 8 / kLinThreads;
+    int k_lo, k_hi;
+    linear_rank_share(r, ksplit, q, k_lo, k_hi);
+    const int gn = k_hi - k_lo < kLinRG ? k_hi - k_lo : kLinRG;
+#pragma unroll
+    for (int u = 0; u < kPieces; ++u) {
+        const int pid = threadIdx.x + u * kLinThreads;
+        const int il = pid / (BN / 8), c8 = pid % (BN / 8);
+        const int a = s_aid[il];
+        const int col = n0 + c8 * 8;
+        const bool on = a >= 0 && col < H2;
+        const typename DT::storage* bp = B_stack + ((long long)(on ? a : 0) * r + k_lo) * H2 + col;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+            pre[u][d] = (on && d < gn) ? load16(bp + (long long)d * H2) : make_uint4(0, 0, 0, 0);
+    }
+}
+
+// kPre: pre holds the first four ranks' B rows (linear_prefetch_b).
+template <typename DT, int BM, int BN, int TP, bool kCoherent = false, bool kPre = false>
 __device__ __forceinline__ void linear_finish(
     const float* s_t, int* s_aid, float* s_v, const int* s_seg, const int* s_ids, int* s_last,
     bool seg_lds, typename DT::storage* __restrict__ y,
@@ -156,7 +202,8 @@ __device__ __forceinline__ void linear_finish(
     long long vstride, int vsplit, const int* __restrict__ seg_indptr,
     const int* __restrict__ adapter_ids, int S, int M, int num_adapters, int H2, int r,
     float scale, float* __restrict__ part, int* __restrict__ counters, int counter_stride,
-    int ksplit, int q, int t, int m0, int n0) {
+    int ksplit, int q, int t, int m0, int n0,
+    const uint4 (&pre)[BM * BN / 8 / kLinThreads][4]) {
     constexpr int kPieces = BM * BN / 8 / kLinThreads;
     static_assert(BM * BN % (8 * kLinThreads) == 0, "uneven epilogue");
     const int tid = threadIdx.x;
@@ -188,7 +235,9 @@ __device__ __forceinline__ void linear_finish(
                 float sum = 0.f;
                 if (s_aid[il] >= 0) {
                     // chunk order, eight loads in flight
-                    sum = sum_partials(vpart + (long long)(m0 + il) * r + g0 + kk, vstride, vsplit);
+                    const float* p = vpart + (long long)(m0 + il) * r + g0 + kk;
+                    sum = kCoherent ? sum_partials_coherent(const_cast<float*>(p), vstride, vsplit)
+                                    : sum_partials(p, vstride, vsplit);
                 }
                 s_v[il * kLinRG + kk] = sum;
             }
@@ -206,10 +255,15 @@ __device__ __forceinline__ void linear_finish(
             // ranks in order, four B rows in flight at a time
             for (int k0 = 0; k0 < gn; k0 += 4) {
                 uint4 braw[4];
+                if (kPre && g0 == k_lo && k0 == 0) {
 #pragma unroll
-                for (int d = 0; d < 4; ++d)
-                    braw[d] = k0 + d < gn ? load16(bp + (long long)(k0 + d) * H2)
-                                          : make_uint4(0, 0, 0, 0);
+                    for (int d = 0; d < 4; ++d) braw[d] = pre[u][d];
+                } else {
+#pragma unroll
+                    for (int d = 0; d < 4; ++d)
+                        braw[d] = k0 + d < gn ? load16(bp + (long long)(k0 + d) * H2)
+                                              : make_uint4(0, 0, 0, 0);
+                }
 #pragma unroll
                 for (int d = 0; d < 4; ++d) {
                     if (k0 + d < gn) {
@@ -304,11 +358,145 @@ __device__ __forceinline__ void linear_finish(
     }
 }
 
+// One row's partial sum of v = x A_a over [h_lo, h_hi) (multiples of 8) on
+// the matrix cores, staged through s_raw (32 KB): one LDS chunk of A
+// (shrink_chunk_mfma) or, for longer ranges, the streaming form
+// (shrink_long_mfma).  Calls emit(k, value) once per k < R from thread k;
+// an empty range emits nothing.  The shrink workgroups and the fallback
+// both take their partials from here, so their bits agree.
+template <typename DT, int R, typename Emit>
+__device__ __forceinline__ void linear_row_partial(const typename DT::storage* __restrict__ A,
+                                                   const typename DT::storage* __restrict__ xr,
+                                                   int H1, int h_lo, int h_hi,
+                                                   unsigned char* s_raw, Emit&& emit) {
+    constexpr int KC = 16384 / R < 512 ? 16384 / R : 512;  // A chunk within 32 KB of LDS
+    uint16_t* s_a = reinterpret_cast<uint16_t*>(s_raw);
+    float* s_red = reinterpret_cast<float*>(s_raw);
+    auto e = [&](int, int k, float v) { emit(k, v); };
+    if (h_hi <= h_lo) return;
+    if (h_hi - h_lo <= KC)
+        shrink_chunk_mfma<DT, R, true, KC>(A, xr, 1, H1, h_lo, h_hi, s_a, s_red, e);
+    else
+        shrink_long_mfma<DT, R, KC>(A, xr, 1, H1, h_lo, h_hi, s_a, s_red, e);
+}
+
+// A shrink workgroup of the one-launch layer (decode shapes): item s is
+// row s / ksplit over K range s % ksplit -- the ranges the tile workgroups
+// split W over -- and publishes that partial of the row's v (zeros for a
+// row without an adapter), then counts itself in on fold_cnt.  It never
+// waits, and the shrink workgroups come first in the grid, so the tile
+// workgroups that wait for them always see them finish.
+template <typename DT>
+__device__ __forceinline__ void linear_shrink_item(
+    int s, const typename DT::storage* __restrict__ x,
+    const typename DT::storage* __restrict__ A_stack, float* __restrict__ vpart,
+    long long vstride, const int* __restrict__ seg_indptr, const int* __restrict__ adapter_ids,
+    int S, int M, int num_adapters, int H1, int r, int ksplit, int chunks_per_split,
+    unsigned char* s_raw, float* s_fv, int* s_seg, int* s_ids, int* s_row_aid, int* fold_cnt,
+    int fold_total) {
+    const int tid = threadIdx.x;
+    const int row = s / ksplit, qq = s - row * ksplit;
+    // The row's adapter: the table through LDS (one coalesced read) when it
+    // fits, else a search in global memory.
+    if (S <= kLinSegLds) {
+        for (int e = tid; e <= S; e += kLinThreads) s_seg[e] = seg_indptr[e];
+        for (int e = tid; e < S; e += kLinThreads) s_ids[e] = adapter_ids[e];
+        __syncthreads();
+        if (tid == 0)
+            *s_row_aid = row < M ? row_adapter((const int*)s_seg, (const int*)s_ids, S, row,
+                                               num_adapters)
+                                 : -1;
+    } else if (tid == 0) {
+        *s_row_aid = row < M ? row_adapter(seg_indptr, adapter_ids, S, row, num_adapters) : -1;
+    }
+    __syncthreads();
+    const int a = *s_row_aid;
+    const int h_lo = qq * chunks_per_split * kLinBK;
+    const int h_hi = min(H1, h_lo + chunks_per_split * kLinBK);
+    float* out = vpart + (long long)qq * vstride + (long long)row * r;
+    auto emit = [&](int k, float v) { s_fv[k] = v; };
+    if (a >= 0) {
+        const typename DT::storage* xr = x + (long long)row * H1;
+        switch (r) {
+            case 16:
+                linear_row_partial<DT, 16>(A_stack + (long long)a * H1 * 16, xr, H1, h_lo, h_hi,
+                                           s_raw, emit);
+                break;
+            case 32:
+                linear_row_partial<DT, 32>(A_stack + (long long)a * H1 * 32, xr, H1, h_lo, h_hi,
+                                           s_raw, emit);
+                break;
+            case 64:
+                linear_row_partial<DT, 64>(A_stack + (long long)a * H1 * 64, xr, H1, h_lo, h_hi,
+                                           s_raw, emit);
+                break;
+            default:
+                linear_row_partial<DT, 128>(A_stack + (long long)a * H1 * 128, xr, H1, h_lo,
+                                            h_hi, s_raw, emit);
+                break;
+        }
+    }
+    // Each value was written by the thread that stores it (emit(k) is
+    // called from thread k).
+    if (row < M)
+        for (int k = tid; k < r; k += kLinThreads)
+            store_partial(out + k, (a >= 0 && h_hi > h_lo) ? s_fv[k] : 0.f);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // every wave's partial stores have completed
+    if (tid == 0) depart(fold_cnt, 1, fold_total);
+}
+
+// The folded shrink's fallback when its wait gives up: v for the tile's
+// rows and this workgroup's first pass of ranks, from x and A with the
+// shrink workgroups' arithmetic -- each K range's partial by
+// linear_row_partial, then the partials added in K-range order starting
+// from zero, as linear_prepare_v sums them -- so the result does not depend
+// on whether the wait succeeded.  Slow (one row and one K range at a time);
+// it uses the staging buffers, so it runs between the main loop and the
+// tile.
+template <typename DT, int R>
+__device__ __forceinline__ void linear_v_refold(
+    float* s_v, float* s_fv, const int* s_aid, const typename DT::storage* __restrict__ x,
+    const typename DT::storage* __restrict__ A_stack, unsigned char* s_raw, int M, int H1,
+    int m0, int BM, int ksplit, int chunks_per_split, int q) {
+    const int tid = threadIdx.x;
+    int k_lo, k_hi;
+    linear_rank_share(R, ksplit, q, k_lo, k_hi);
+    const int gn = k_hi - k_lo < kLinRG ? k_hi - k_lo : kLinRG;
+    for (int il = 0; il < BM; ++il) {
+        const int a = m0 + il < M ? s_aid[il] : -1;
+        float sum = 0.f;  // thread k < R: rank k of this row
+        if (a >= 0) {
+            const typename DT::storage* A = A_stack + (long long)a * H1 * R;
+            const typename DT::storage* xr = x + (long long)(m0 + il) * H1;
+            for (int qq = 0; qq < ksplit; ++qq) {
+                const int h_lo = qq * chunks_per_split * kLinBK;
+                const int h_hi = min(H1, h_lo + chunks_per_split * kLinBK);
+                linear_row_partial<DT, R>(A, xr, H1, h_lo, h_hi, s_raw,
+                                          [&](int k, float v) { s_fv[k] = v; });
+                if (tid < R) sum += h_hi > h_lo ? s_fv[tid] : 0.f;
+                __syncthreads();  // s_fv read before the next range writes it
+            }
+        }
+        if (tid >= k_lo && tid < k_lo + gn) s_v[il * kLinRG + tid - k_lo] = sum;
+    }
+}
+
 // Grid: tiles * ksplit workgroups (rounded up; the extra ones return at
 // once), workgroup b taking K range q = b % ksplit of tile b / ksplit.  With
 // ksplit a multiple of the 8 XCDs, which receive workgroups round-robin,
 // every XCD then streams one K range of x for all tiles.
-template <typename DT, typename SH>
+//
+// kFold: the shrink runs inside this launch.  The first n_shrink workgroups
+// are shrink workgroups (linear_shrink_item; v's partials are then the K
+// ranges', vsplit == ksplit) and count themselves in on fold_cnt (low 16
+// bits); each tile workgroup after them waits for all of them once its
+// main loop is done, reads its v, and counts itself out (high bits; the
+// participant completing the total returns the counter to zero).  Past
+// wait_ticks a tile workgroup recomputes its v (linear_v_refold, same
+// bits) and raises the sticky flag.
+template <typename DT, typename SH, bool kFold = false>
 __global__ __launch_bounds__(kLinThreads) void linear_lora_kernel(
     typename DT::storage* __restrict__ y, const typename DT::storage* __restrict__ x,
     const typename DT::storage* __restrict__ W, const typename DT::storage* __restrict__ bias,
@@ -316,7 +504,9 @@ __global__ __launch_bounds__(kLinThreads) void linear_lora_kernel(
     long long vstride, int vsplit, const int* __restrict__ seg_indptr,
     const int* __restrict__ adapter_ids, int S, int M, int num_adapters, int H1, int H2, int r,
     float scale, float* __restrict__ part, int* __restrict__ counters, int counter_stride,
-    int ksplit, int chunks_per_split, int tiles_n, int tiles) {
+    int ksplit, int chunks_per_split, int tiles_n, int tiles,
+    const typename DT::storage* __restrict__ A_stack, int* __restrict__ fold_cnt,
+    int* __restrict__ flag, long long wait_ticks, int n_shrink) {
     constexpr int BM = SH::kBM, BN = SH::kBN, XP = SH::kXP, WP = SH::kWP, PD = SH::kD;
     constexpr int TM = SH::TM, TN = SH::TN, TP = SH::kTP;
     __shared__ __attribute__((aligned(16))) unsigned char s_raw[SH::kLdsBytes];
@@ -325,15 +515,29 @@ __global__ __launch_bounds__(kLinThreads) void linear_lora_kernel(
     __shared__ int s_seg[kLinSegLds + 1];
     __shared__ int s_ids[kLinSegLds];
     __shared__ int s_last;
+    __shared__ int s_fold_ok;
+    __shared__ float s_fv[kFold ? 128 : 1];  // one row's v partial (folded shrink)
+    __shared__ int s_row_aid;
     uint16_t* s_stage = reinterpret_cast<uint16_t*>(s_raw);
     float* s_t = reinterpret_cast<float*>(s_raw);
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wid = tid / kWave;
-    const int q = (int)(blockIdx.x % (unsigned)ksplit);
-    const int t = (int)(blockIdx.x / (unsigned)ksplit);
-    if (t >= tiles) return;  // whole workgroup
+    const int fold_total = n_shrink + (((int)gridDim.x - n_shrink) << 16);
+    if constexpr (kFold) {
+        if ((int)blockIdx.x < n_shrink) {
+            linear_shrink_item<DT>((int)blockIdx.x, x, A_stack, const_cast<float*>(vpart),
+                                   vstride, seg_indptr, adapter_ids, S, M, num_adapters, H1, r,
+                                   ksplit, chunks_per_split, s_raw, s_fv, s_seg, s_ids,
+                                   &s_row_aid, fold_cnt, fold_total);
+            return;
+        }
+    }
+    const unsigned b = blockIdx.x - (unsigned)n_shrink;
+    const int q = (int)(b % (unsigned)ksplit);
+    const int t = (int)(b / (unsigned)ksplit);
+    if (t >= tiles) return;  // whole workgroup (never in the folded grid, which is exact)
     const int m0 = (t / tiles_n) * BM;
     const int n0 = (t % tiles_n) * BN;
     const int k_begin = q * chunks_per_split * kLinBK;
@@ -441,8 +645,9 @@ __global__ __launch_bounds__(kLinThreads) void linear_lora_kernel(
         if (seg_lds && e < S) s_ids[e] = ids_r[u];
     }
     lds_barrier();
-    linear_prepare(s_aid, s_v, s_seg, s_ids, seg_lds, vpart, vstride, vsplit, seg_indptr,
-                   adapter_ids, S, M, num_adapters, r, ksplit, q, m0, BM);
+    linear_prepare<false, !kFold>(s_aid, s_v, s_seg, s_ids, seg_lds, vpart, vstride, vsplit,
+                                  seg_indptr, adapter_ids, S, M, num_adapters, r, ksplit, q, m0,
+                                  BM);
 
     for (int c0 = 0; c0 < nchunks; c0 += PD) {
 #pragma unroll
@@ -458,6 +663,42 @@ __global__ __launch_bounds__(kLinThreads) void linear_lora_kernel(
     }
     __syncthreads();  // every wave is done with the staging buffers
 
+    // Folded: the correction's first B rows requested now, then the wait
+    // for every shrink workgroup and this workgroup's first pass of v (or,
+    // past the patience, v recomputed); the B loads overlap both.
+    uint4 bpre[BM * BN / 8 / kLinThreads][4];
+    if constexpr (kFold)
+        linear_prefetch_b<DT, BM, BN>(bpre, s_aid, B_stack, H2, r, ksplit, q, n0);
+    if constexpr (kFold) {
+        if (tid == 0) s_fold_ok = wait_for_producers(fold_cnt, n_shrink, wait_ticks);
+        __syncthreads();
+        if (s_fold_ok) {
+            linear_prepare_v<true>(s_v, vpart, vstride, vsplit, M, r, ksplit, q, m0, BM);
+        } else {
+            if (tid == 0) __hip_atomic_store(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            switch (r) {
+                case 16:
+                    linear_v_refold<DT, 16>(s_v, s_fv, s_aid, x, A_stack, s_raw, M, H1, m0, BM,
+                                            ksplit, chunks_per_split, q);
+                    break;
+                case 32:
+                    linear_v_refold<DT, 32>(s_v, s_fv, s_aid, x, A_stack, s_raw, M, H1, m0, BM,
+                                            ksplit, chunks_per_split, q);
+                    break;
+                case 64:
+                    linear_v_refold<DT, 64>(s_v, s_fv, s_aid, x, A_stack, s_raw, M, H1, m0, BM,
+                                            ksplit, chunks_per_split, q);
+                    break;
+                default:
+                    linear_v_refold<DT, 128>(s_v, s_fv, s_aid, x, A_stack, s_raw, M, H1, m0, BM,
+                                             ksplit, chunks_per_split, q);
+                    break;
+            }
+        }
+        __syncthreads();  // every thread's v loads have returned
+        if (tid == 0) depart(fold_cnt, 1 << 16, fold_total);
+    }
+
     // ---- accumulators -> float tile in LDS -------------------------------
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -467,10 +708,10 @@ __global__ __launch_bounds__(kLinThreads) void linear_lora_kernel(
             for (int e = 0; e < 4; ++e)
                 s_t[(wr0 + 16 * i + 4 * lg + e) * TP + wc0 + 16 * j + lr] = acc[i][j][e];
 
-    linear_finish<DT, BM, BN, TP>(s_t, s_aid, s_v, s_seg, s_ids, &s_last, seg_lds, y, bias, B_stack,
-                                  vpart, vstride, vsplit, seg_indptr, adapter_ids, S, M,
-                                  num_adapters, H2, r, scale, part, counters, counter_stride,
-                                  ksplit, q, t, m0, n0);
+    linear_finish<DT, BM, BN, TP, kFold, kFold>(
+        s_t, s_aid, s_v, s_seg, s_ids, &s_last, seg_lds, y, bias, B_stack, vpart, vstride, vsplit,
+        seg_indptr, adapter_ids, S, M, num_adapters, H2, r, scale, part, counters, counter_stride,
+        ksplit, q, t, m0, n0, bpre);
 }
 
 // Any shape and dtype: one thread per output element, the base product as

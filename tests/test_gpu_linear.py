@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 import workloads as wl
-from gpu_helpers import assert_close, to_device, torch_dtype
+from gpu_helpers import COUNTER_BYTES, assert_close, to_device, torch_dtype
 
 pytestmark = pytest.mark.gpu
 
@@ -36,15 +36,25 @@ def _dev(a, dtype, device="cuda:0"):
     return torch.from_numpy(np.ascontiguousarray(a)).to(device=device).to(torch_dtype(dtype))
 
 
-def _gpu_linear(w, W, b, d=None, seg=None, ids=None):
+def _gpu_linear(w, W, b, d=None, seg=None, ids=None, expect_flag=0):
+    """lora_linear on a fresh zeroed workspace.  Afterwards every counter
+    (the split-K tile counters and the folded shrink's) must be back at zero
+    and the sticky flag (a folded workgroup gave up waiting for the others'
+    shares of v) must read `expect_flag`."""
     import torch
     import segmented_gather_gemv_sgmv_amd as sg
     d = to_device(w) if d is None else d
     seg = d["seg"] if seg is None else seg
     ids = d["ids"] if ids is None else ids
+    need = sg.lora_linear_workspace_bytes(w.num_rows, int(seg.numel()) - 1, w.H1, w.H2, w.r,
+                                          torch_dtype(w.dtype))
+    ws = torch.zeros(max(need, COUNTER_BYTES), dtype=torch.uint8, device="cuda:0")
     y = sg.lora_linear(d["x"], _dev(W, w.dtype), d["A"], d["B"], seg, ids, w.scale,
-                       bias=_dev(b, w.dtype))
+                       bias=_dev(b, w.dtype), workspace=ws)
     torch.cuda.synchronize()
+    counters = ws[:COUNTER_BYTES].view(torch.int32)
+    assert int(counters[-1].item()) == expect_flag, "sticky flag"
+    assert int(counters[:-1].abs().sum().item()) == 0, "counters not returned to zero"
     return y.double().cpu().numpy()
 
 
@@ -188,6 +198,28 @@ def test_prefill_full_size_sampled_rows():
         ref = oracle.lora_linear(w.x[i:i + 1], W, b, w.A, w.B, np.array([0, 1], np.int32),
                                  ids[s:s + 1], w.scale)
         assert_close(got[i:i + 1], ref, w.dtype, f"row {i}")
+
+
+@pytest.mark.parametrize("dtype,R,H1,H2,r", [("f16", 64, 256, 256, 16), ("bf16", 37, 512, 328, 16),
+                                             ("f16", 20, 1024, 200, 32), ("bf16", 9, 2048, 64, 64)])
+def test_folded_shrink_fallback_is_bit_identical(dtype, R, H1, H2, r):
+    """Decode shapes fold the shrink into the tile launch: each workgroup
+    publishes a share of v and waits for the others' before its correction.
+    With no patience every workgroup recomputes its v itself; the result
+    must be the same bits, the sticky flag set and the counters back at
+    zero."""
+    import segmented_gather_gemv_sgmv_amd as sg
+    w = wl.small_random(31, dtype, H1, H2, r, 6, R, max(1, R // 2))
+    W, b = wl.base_layer(31, dtype, H1, H2)
+    d = to_device(w)
+    normal = _gpu_linear(w, W, b, d)
+    try:
+        sg.set_fused_wait(0.0)
+        alone = _gpu_linear(w, W, b, d, expect_flag=1)
+    finally:
+        sg.set_fused_wait(0.02)
+    assert np.array_equal(normal, alone)
+    assert_close(normal, _oracle(w, W, b), dtype, "folded", _oracle(w, W, b, absolute=True))
 
 
 def test_repeated_calls_are_bitwise_identical():
