@@ -688,11 +688,58 @@ __global__ __launch_bounds__(kMixedThreads, 4) void lora_mixed_kernel(
     const typename DT::storage* __restrict__ B_stack, const int* __restrict__ seg_indptr,
     const int* __restrict__ adapter_ids, int S, int num_rows, int num_adapters, int H1, int H2,
     float scale, float* __restrict__ partials, int* __restrict__ counters, MixedSplit sp,
-    int n_counters, int counter_stride, long long wait_ticks) {
+    int n_counters, int counter_stride, long long wait_ticks, int guess) {
     using C = MixedClasses<LP, SP, GP>;
     constexpr int NW = kMixedThreads / kWave;
     __shared__ __align__(16) unsigned char s_mem[C::kLdsBytes];
     __shared__ int s_scan[kMixedScanInts];
+    // guess (the host sets it when num_rows == S, a decode batch): segment i
+    // is taken to be row i alone, a one-row tile of the single class, so a
+    // shrink item streams its chunk of A before the scan below would have
+    // named it.  The guess is checked -- every segment one row, in order,
+    // with an adapter in range, the same table for every workgroup -- before
+    // anything is published; if it fails, the item runs the scanned path.
+    if (guess && (int)blockIdx.x < S * sp.k[2]) {  // block-uniform
+        const int tid = threadIdx.x;
+        int raw_seg[kMixedPasses], raw_id[kMixedPasses];
+#pragma unroll
+        for (int p = 0; p < kMixedPasses; ++p) {  // in flight beside the A chunk
+            const int j = p * kMixedThreads + tid;
+            raw_seg[p] = seg_indptr[min(j, S)];
+            raw_id[p] = adapter_ids[min(j, S - 1)];
+        }
+        const int ti = (int)blockIdx.x / sp.k[2];
+        const int sub = (int)blockIdx.x - ti * sp.k[2];
+        const int a_raw = adapter_ids[ti];
+        Tile t;
+        t.row0 = ti;
+        t.nrows = 1;
+        t.adapter = (a_raw >= 0 && a_raw < num_adapters) ? a_raw : 0;  // an address in range
+        t.seg = ti;
+        float* s_sv = reinterpret_cast<float*>(s_mem) + GP::kRedFloats;
+        const int h_lo = sub * sp.h[2];
+        const int h_hi = min(H1, h_lo + sp.h[2]);
+        GP::shrink_range(t, x, A_stack, H1, h_lo, h_hi, s_mem,
+                         [&](int, int k, float v) { s_sv[k] = v; });
+        bool ok = true;
+#pragma unroll
+        for (int p = 0; p < kMixedPasses; ++p) {
+            const int j = p * kMixedThreads + tid;
+            if (j <= S) ok = ok && raw_seg[p] == j;
+            if (j < S) ok = ok && raw_id[p] >= 0 && raw_id[p] < num_adapters;
+        }
+        if (__syncthreads_and(ok)) {
+            float* out = partials + (long long)sub * num_rows * R + (long long)ti * R;
+            for (int k = tid; k < R; k += kMixedThreads) store_partial(&out[k], s_sv[k]);
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (tid == 0)
+                depart(&counters[(long long)ti * counter_stride], 1, sp.k[2] + (sp.c[2] << 16));
+            return;
+        }
+        __syncthreads();  // LDS free for the scanned path
+    }
     MixedScan m;
     mixed_scan<C>(seg_indptr, adapter_ids, S, num_rows, num_adapters, s_scan, m);
     const int T0 = m.total[0], T1 = m.total[1], T2 = m.total[2];

@@ -222,6 +222,22 @@ def test_folded_shrink_fallback_is_bit_identical(dtype, R, H1, H2, r):
     assert_close(normal, _oracle(w, W, b), dtype, "folded", _oracle(w, W, b, absolute=True))
 
 
+def test_prefill_tiling_every_row():
+    """Every row of the prefill batch (4096 rows, the same 16 segments and
+    adapters, 128 x 128 tiles) against the oracle, at H1 = 1024 and H2 = 512
+    so that the oracle finishes in seconds: the row tiling, the segment
+    boundaries inside tiles and the ragged last tile are those of the
+    full-size layer, only the K and column extents are shorter."""
+    full = wl.prefill(0)
+    lengths = np.diff(full.seg_indptr)
+    w = wl.make_workload("prefill_tiling_4096x1024x512", "f16", 1024, 512, 16, 16, lengths,
+                         full.adapter_ids, 2.0, rng=np.random.default_rng(7))
+    W, b = wl.base_layer(7, w.dtype, w.H1, w.H2)
+    print("lora_linear prefill tiling 4096 x 1024 -> 512", flush=True)
+    assert_close(_gpu_linear(w, W, b), _oracle(w, W, b), w.dtype, "prefill tiling",
+                 _oracle(w, W, b, absolute=True))
+
+
 def test_repeated_calls_are_bitwise_identical():
     w = wl.small_random(15, "f16", 1024, 512, 16, 16, 64, 64)
     W, b = wl.base_layer(15, "f16", 1024, 512)

@@ -212,6 +212,43 @@ def test_invalid_adapter_ids_are_skipped():
             assert_close(y[rows], y_ref[rows], "f16", f"segment {s}")
 
 
+@pytest.mark.parametrize("kind", ["one_row_each", "empty_and_two_rows", "bad_adapter",
+                                  "offset_start"])
+def test_decode_guess_holds_or_falls_back(kind):
+    """With as many rows as segments, lora_apply's single-launch shrink items
+    guess that segment i is row i alone and stream their A chunk before the
+    segment scan; the guess is checked before anything is published.  Tables
+    of that size where it holds and where it does not (an empty segment next
+    to a two-row one, an adapter id out of range, a table that starts past
+    row 0) must all match the oracle, with the counters back at zero and no
+    fallback of the hand-off."""
+    import torch
+    S, N, H = 48, 7, 1024
+    rng = np.random.default_rng(zlib.crc32(kind.encode()))
+    lengths = np.ones(S, np.int64)
+    if kind == "empty_and_two_rows":
+        lengths[5], lengths[6] = 0, 2
+    ids = rng.integers(0, N, size=S).astype(np.int32)
+    w = wl.make_workload(f"guess_{kind}", "f16", H, H, 16, N, lengths, ids, 1.5, rng=rng)
+    if kind == "offset_start":
+        # row 0 uncovered, segments 0 .. S - 2 one row each, the last empty
+        w.seg_indptr = np.minimum(np.arange(1, S + 2, dtype=np.int32), S)
+    assert w.num_rows == w.num_segments == S
+    good = w.adapter_ids.copy()
+    d = to_device(w)
+    if kind == "bad_adapter":
+        bad = good.copy()
+        bad[S // 2] = N
+        d["ids"] = torch.from_numpy(bad).cuda()
+        good = bad
+    y_ref, _ = oracle.lora_apply(w.y0, w.x, w.A, w.B, w.seg_indptr,
+                                 np.where((good >= 0) & (good < N), good, 0), w.scale)
+    if kind == "bad_adapter":  # the row of the bad segment keeps its y
+        y_ref[S // 2] = w.y0[S // 2]
+    my, _ = magnitude(w)
+    assert_close(gpu_lora_apply(w, d), y_ref, "f16", kind, my)
+
+
 def test_misaligned_pointers_take_general_path():
     import torch
     import segmented_gather_gemv_sgmv_amd as sg
