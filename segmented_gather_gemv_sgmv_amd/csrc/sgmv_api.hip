@@ -1101,8 +1101,10 @@ int lora_apply(void* y, const void* x, const void* A_stack, const void* B_stack,
                     using SP = decltype(sp_);
                     using GP = decltype(gp);
                     if (!xp.two) {
-                        // as many rows as segments: guess one row per segment
-                        const int guess = num_rows == num_segments ? 1 : 0;
+                        // as many rows as segments: guess one row per
+                        // segment; one segment: guess it covers every row
+                        const int guess =
+                            num_rows == num_segments ? 1 : (num_segments == 1 ? 2 : 0);
                         launch(&lora_mixed_kernel<DT, R, LP, SP, GP>, dim3((unsigned)xp.grid_one),
                                dim3(kMixedThreads), st, (T*)y, (const T*)x, (const T*)A_stack,
                                (const T*)B_stack, seg_indptr, adapter_ids, num_segments, num_rows,

@@ -112,6 +112,10 @@ struct VecTile {
     static constexpr int kLdsBytes = (kRedFloats + RB * R) * 4 + 16;
     static_assert(R % kVec == 0 && kWave % LPR == 0, "vector rank");
 
+    __device__ static __forceinline__ float* s_v(unsigned char* lds) {
+        return reinterpret_cast<float*>(lds) + kRedFloats;
+    }
+
     template <typename Emit>
     __device__ static __forceinline__ void shrink_range(const Tile& t, const st* __restrict__ x,
                                                         const st* __restrict__ A_stack, int H1,
@@ -693,52 +697,80 @@ __global__ __launch_bounds__(kMixedThreads, 4) void lora_mixed_kernel(
     constexpr int NW = kMixedThreads / kWave;
     __shared__ __align__(16) unsigned char s_mem[C::kLdsBytes];
     __shared__ int s_scan[kMixedScanInts];
-    // guess (the host sets it when num_rows == S, a decode batch): segment i
-    // is taken to be row i alone, a one-row tile of the single class, so a
-    // shrink item streams its chunk of A before the scan below would have
-    // named it.  The guess is checked -- every segment one row, in order,
-    // with an adapter in range, the same table for every workgroup -- before
-    // anything is published; if it fails, the item runs the scanned path.
-    if (guess && (int)blockIdx.x < S * sp.k[2]) {  // block-uniform
-        const int tid = threadIdx.x;
-        int raw_seg[kMixedPasses], raw_id[kMixedPasses];
+    // guess: a table shape the host expects, so that a shrink item streams
+    // its chunk of A before the scan below would have named it.  1 (as many
+    // rows as segments, a decode batch): segment i is row i alone, a one-row
+    // tile of the single class.  2 (one segment): the segment is every row,
+    // cut into tiles of its class.  The guess is checked -- the whole table
+    // as guessed, adapters in range, the same table for every workgroup --
+    // before anything is published; if it fails, the item runs the scanned
+    // path.
+    if (guess) {
+        int gc, gT;  // the guessed class of every tile, and its tile count
+        if (guess == 1) {
+            gc = 2;
+            gT = S;
+        } else {
+            gc = num_rows >= C::kTH ? 0 : (num_rows >= 2 ? 1 : 2);
+            gT = C::tiles(gc, num_rows);
+        }
+        if ((int)blockIdx.x < gT * sp.k[gc]) {  // block-uniform
+            auto guessed = [&](auto pol) -> bool {
+                using P = decltype(pol);
+                if constexpr (IsNoTile<P>::value) {
+                    return false;
+                } else {
+                    const int tid = threadIdx.x;
+                    int raw_seg[kMixedPasses], raw_id[kMixedPasses];
 #pragma unroll
-        for (int p = 0; p < kMixedPasses; ++p) {  // in flight beside the A chunk
-            const int j = p * kMixedThreads + tid;
-            raw_seg[p] = seg_indptr[min(j, S)];
-            raw_id[p] = adapter_ids[min(j, S - 1)];
-        }
-        const int ti = (int)blockIdx.x / sp.k[2];
-        const int sub = (int)blockIdx.x - ti * sp.k[2];
-        const int a_raw = adapter_ids[ti];
-        Tile t;
-        t.row0 = ti;
-        t.nrows = 1;
-        t.adapter = (a_raw >= 0 && a_raw < num_adapters) ? a_raw : 0;  // an address in range
-        t.seg = ti;
-        float* s_sv = reinterpret_cast<float*>(s_mem) + GP::kRedFloats;
-        const int h_lo = sub * sp.h[2];
-        const int h_hi = min(H1, h_lo + sp.h[2]);
-        GP::shrink_range(t, x, A_stack, H1, h_lo, h_hi, s_mem,
-                         [&](int, int k, float v) { s_sv[k] = v; });
-        bool ok = true;
+                    for (int p = 0; p < kMixedPasses; ++p) {  // in flight beside the A chunk
+                        const int j = p * kMixedThreads + tid;
+                        raw_seg[p] = seg_indptr[min(j, S)];
+                        raw_id[p] = adapter_ids[min(j, S - 1)];
+                    }
+                    const int ti = (int)blockIdx.x / sp.k[gc];
+                    const int sub = (int)blockIdx.x - ti * sp.k[gc];
+                    const int h = C::height(gc);
+                    Tile t;
+                    t.row0 = guess == 1 ? ti : ti * h;
+                    t.nrows = guess == 1 ? 1 : min(h, num_rows - t.row0);
+                    const int a_raw = adapter_ids[guess == 1 ? ti : 0];
+                    t.adapter = (a_raw >= 0 && a_raw < num_adapters) ? a_raw : 0;  // in range
+                    t.seg = guess == 1 ? ti : 0;
+                    float* s_gv = P::s_v(s_mem);
+                    const int h_lo = sub * sp.h[gc];
+                    const int h_hi = min(H1, h_lo + sp.h[gc]);
+                    P::shrink_range(t, x, A_stack, H1, h_lo, h_hi, s_mem,
+                                    [&](int i, int k, float v) { s_gv[i * R + k] = v; });
+                    bool ok = true;
 #pragma unroll
-        for (int p = 0; p < kMixedPasses; ++p) {
-            const int j = p * kMixedThreads + tid;
-            if (j <= S) ok = ok && raw_seg[p] == j;
-            if (j < S) ok = ok && raw_id[p] >= 0 && raw_id[p] < num_adapters;
+                    for (int p = 0; p < kMixedPasses; ++p) {
+                        const int j = p * kMixedThreads + tid;
+                        const int want = guess == 1 ? j : (j == 0 ? 0 : num_rows);
+                        if (j <= S) ok = ok && raw_seg[p] == want;
+                        if (j < S) ok = ok && raw_id[p] >= 0 && raw_id[p] < num_adapters;
+                    }
+                    if (!__syncthreads_and(ok)) {
+                        __syncthreads();  // LDS free for the scanned path
+                        return false;
+                    }
+                    float* out = partials + (long long)sub * num_rows * R + (long long)t.row0 * R;
+                    for (int e = tid; e < t.nrows * R; e += kMixedThreads)
+                        store_partial(&out[e], s_gv[e]);
+                    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                    __builtin_amdgcn_s_waitcnt(0);
+                    __syncthreads();
+                    // every other class is empty, so tile ti has counter slot ti
+                    if (tid == 0)
+                        depart(&counters[(long long)ti * counter_stride], 1,
+                               sp.k[gc] + (sp.c[gc] << 16));
+                    return true;
+                }
+            };
+            const bool done =
+                gc == 0 ? guessed(LP{}) : (gc == 1 ? guessed(SP{}) : guessed(GP{}));
+            if (done) return;
         }
-        if (__syncthreads_and(ok)) {
-            float* out = partials + (long long)sub * num_rows * R + (long long)ti * R;
-            for (int k = tid; k < R; k += kMixedThreads) store_partial(&out[k], s_sv[k]);
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            if (tid == 0)
-                depart(&counters[(long long)ti * counter_stride], 1, sp.k[2] + (sp.c[2] << 16));
-            return;
-        }
-        __syncthreads();  // LDS free for the scanned path
     }
     MixedScan m;
     mixed_scan<C>(seg_indptr, adapter_ids, S, num_rows, num_adapters, s_scan, m);

@@ -249,6 +249,35 @@ def test_decode_guess_holds_or_falls_back(kind):
     assert_close(gpu_lora_apply(w, d), y_ref, "f16", kind, my)
 
 
+@pytest.mark.parametrize("kind,dtype,r,R", [
+    ("all_rows", "f16", 16, 128), ("all_rows", "f32", 8, 14), ("all_rows", "bf16", 64, 40),
+    ("short_end", "f16", 16, 128), ("late_start", "f16", 16, 100), ("bad_adapter", "f16", 16, 64)])
+def test_single_segment_guess_holds_or_falls_back(kind, dtype, r, R):
+    """With one segment, lora_apply's single-launch shrink items guess that
+    it covers every row (tiles of its class) and stream their A chunk before
+    the segment scan; the guess is checked before anything is published.
+    Segments that do cover every row, that stop short of the last rows, that
+    start past row 0, or that name an adapter out of range must all match
+    the oracle, with the counters back at zero and no fallback."""
+    import torch
+    N, H = 5, 512
+    rng = np.random.default_rng(zlib.crc32(f"{kind}{dtype}{r}{R}".encode()))
+    w = wl.make_workload(f"one_{kind}", dtype, H, H, r, N, [R], [3], 1.25, rng=rng)
+    if kind == "short_end":
+        w.seg_indptr = np.array([0, R - 3], np.int32)
+    elif kind == "late_start":
+        w.seg_indptr = np.array([2, R], np.int32)
+    d = to_device(w)
+    ids = w.adapter_ids.copy()
+    if kind == "bad_adapter":
+        d["ids"] = torch.tensor([N], dtype=torch.int32, device="cuda")
+    y_ref, _ = oracle.lora_apply(w.y0, w.x, w.A, w.B, w.seg_indptr, ids, w.scale)
+    if kind == "bad_adapter":
+        y_ref = w.y0.astype(np.float64)
+    my, _ = magnitude(w)
+    assert_close(gpu_lora_apply(w, d), y_ref, dtype, kind, my)
+
+
 def test_misaligned_pointers_take_general_path():
     import torch
     import segmented_gather_gemv_sgmv_amd as sg
