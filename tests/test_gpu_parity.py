@@ -278,6 +278,29 @@ def test_single_segment_guess_holds_or_falls_back(kind, dtype, r, R):
     assert_close(gpu_lora_apply(w, d), y_ref, dtype, kind, my)
 
 
+@pytest.mark.parametrize("shape", ["rows_eq_segments", "one_segment"])
+@pytest.mark.parametrize("dtype,r,H", [("f32", 4, 512), ("f32", 16, 768), ("bf16", 8, 1024),
+                                       ("bf16", 16, 1024), ("f16", 32, 512), ("bf16", 64, 1024),
+                                       ("f16", 128, 512)])
+def test_guessed_tables_across_dtypes_and_ranks(shape, dtype, r, H):
+    """Both guessed table shapes (one row per segment; one segment over every
+    row) on every class a dtype and rank can put them in: one-row vector
+    tiles, 4-row vector tiles (float32, rank 8, ranks >= 64 below 16 rows),
+    MFMA tiles."""
+    N = 6
+    rng = np.random.default_rng(zlib.crc32(f"{shape}{dtype}{r}{H}".encode()))
+    if shape == "rows_eq_segments":
+        R = 40
+        lengths, ids = np.ones(R, np.int64), rng.integers(0, N, size=R).astype(np.int32)
+    else:
+        R = 37 if r < 64 else 13  # ragged last tile; at r >= 64 below the MFMA threshold
+        lengths, ids = [R], [int(rng.integers(0, N))]
+    w = wl.make_workload(f"guess_{shape}", dtype, H, H, r, N, lengths, ids, 0.75, rng=rng)
+    y_ref, _ = oracle.lora_apply(w.y0, w.x, w.A, w.B, w.seg_indptr, w.adapter_ids, w.scale)
+    my, _ = magnitude(w)
+    assert_close(gpu_lora_apply(w), y_ref, dtype, f"{shape} {dtype} r{r}", my)
+
+
 def test_misaligned_pointers_take_general_path():
     import torch
     import segmented_gather_gemv_sgmv_amd as sg
@@ -306,12 +329,15 @@ def test_repeated_calls_are_bitwise_identical():
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("which", ["skewed", "decode_guess", "one_segment_guess"])
+def test_graph_replay_matches_eager(which):
     """lora_apply captured in a HIP graph: every replay, with eager work and
-    synchronisations in between, equals the eager result."""
+    synchronisations in between, equals the eager result (a scanned table
+    and both guessed ones)."""
     import torch
     import segmented_gather_gemv_sgmv_amd as sg
-    w = wl.config(2)
+    w = {"skewed": lambda: wl.config(2), "decode_guess": lambda: wl.config(1),
+         "one_segment_guess": lambda: wl.config(2, control=True)}[which]()
     d = to_device(w)
     y_eager = torch.from_numpy(gpu_lora_apply(w, d))
     ws = torch.zeros(sg.lora_apply_workspace_bytes(w.num_rows, w.num_segments, w.H1, w.H2, w.r,
