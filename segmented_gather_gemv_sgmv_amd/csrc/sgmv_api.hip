@@ -382,6 +382,14 @@ MixedSplit mixed_split(const MixedShape& ms, int R, int S, int H1, int H2, bool 
     const int n_targets = one_launch ? 5 : 7;
     MixedSplit sp{};
     for (int c = 0; c < 3; ++c) {
+        if (one_launch && c == 0) {
+            // One-launch MFMA items each take a whole LDS chunk of A (the
+            // coarsest target, capped by the chunk): on the Zipf decode batch
+            // and its one-segment control, half-chunk items (twice the
+            // workgroups) measured 3 % and 2 % slower.
+            mixed_split_class(ms, 0, kTargets[n_targets - 1], H1, H2, true, sp);
+            continue;
+        }
         long long unit_q[3] = {0, 0, 0};
         unit_q[c] = 1;
         const long long tiles_c = mixed_bound(R, S, ms, unit_q);
