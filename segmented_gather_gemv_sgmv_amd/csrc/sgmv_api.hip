@@ -441,6 +441,18 @@ MixedPlan make_mixed_plan(const MixedShape& ms, int R, int S, int H1, int H2) {
     return p;
 }
 
+// The two-launch lora_apply's expand item table (sgmv_mixed.hpp, item_count):
+// grid_expand 16-byte entries and the count, after the largest partials
+// either form of the mixed path writes.
+size_t mixed_table_offset(const MixedPlan& xp, long long num_rows, int r) {
+    const size_t part = (size_t)xp.kmax * (size_t)num_rows * (size_t)r * sizeof(float);
+    return kCounterBytes + ((part + 255) & ~(size_t)255);
+}
+
+size_t mixed_table_end(const MixedPlan& xp, long long num_rows, int r) {
+    return mixed_table_offset(xp, num_rows, r) + (size_t)(xp.grid_expand + 1) * 16;
+}
+
 // Calls f(DT{}, integral_constant<R>{}, LongP{}, ShortP{}, SingleP{}) for the
 // mixed kernels of the dtype and rank (the classes as mixed_shape defines them).
 template <typename F>
@@ -902,11 +914,13 @@ size_t lora_apply_workspace_bytes(int32_t num_rows, int32_t num_segments, int32_
     const MfmaSplitPlan sp = make_mfma_split_plan(mp, H1, H2, r);
     if (sp.ok && sp.ksplit > k) k = sp.ksplit;
     const MixedShape ms = mixed_shape(H1, H2, r, dtype);
+    size_t table = 0;
     if (mixed_takes(ms, num_segments)) {
         const MixedPlan xp = make_mixed_plan(ms, num_rows, num_segments, H1, H2);
         if (xp.ok && xp.kmax > k) k = xp.kmax;
+        if (xp.ok && xp.two) table = mixed_table_end(xp, num_rows, r);
     }
-    return kCounterBytes + (size_t)k * (size_t)num_rows * (size_t)r * sizeof(float);
+    return std::max(table, kCounterBytes + (size_t)k * (size_t)num_rows * (size_t)r * sizeof(float));
 }
 
 int sgmv_shrink(float* v, const void* x, const void* A_stack, const int32_t* seg_indptr,
@@ -956,7 +970,7 @@ int sgmv_shrink(float* v, const void* x, const void* A_stack, const int32_t* seg
                            dim3(kMixedThreads), st, (const T*)x, (const T*)A_stack, seg_indptr,
                            adapter_ids, num_segments, num_rows, num_adapters, H1, part, sp,
                            in_kernel ? v : (float*)nullptr, in_kernel ? (int*)workspace : nullptr,
-                           kCounterStride);
+                           kCounterStride, (int4*)nullptr, 0);
                 });
                 return launch_status();
             }
@@ -1042,7 +1056,7 @@ int sgmv_expand(void* y, const float* v, const void* B_stack, const int32_t* seg
                     launch(&expand_mixed_kernel<DT, R, LP, SP, SplitSingle<DT, R>>, dim3((unsigned)xp.grid_expand),
                            dim3(kMixedThreads), st, (T*)y, (const T*)B_stack, seg_indptr,
                            adapter_ids, num_segments, num_rows, num_adapters, H2, scale, v,
-                           xp.two_sp, 1, 1, 1);
+                           xp.two_sp, 1, 1, 1, (const int4*)nullptr, 0);
                 });
                 return launch_status();
             }
@@ -1120,16 +1134,19 @@ int lora_apply(void* y, const void* x, const void* A_stack, const void* B_stack,
                                kCounterStride, wait, guess);
                         return;
                     }
+                    // the shrink launch writes the expand launch's items
+                    int4* items = (int4*)((char*)workspace + mixed_table_offset(xp, num_rows, r));
+                    const int n_items = (int)xp.grid_expand;
                     launch(&shrink_mixed_kernel<DT, R, LP, SP, GP>, dim3((unsigned)xp.grid_shrink),
                            dim3(kMixedThreads), st, (const T*)x, (const T*)A_stack, seg_indptr,
                            adapter_ids, num_segments, num_rows, num_adapters, H1, part,
-                           xp.two_sp, (float*)nullptr, (int*)nullptr, 0);
+                           xp.two_sp, (float*)nullptr, (int*)nullptr, 0, items, n_items);
                     if (t_pending != hipSuccess) return;  // no expand over unwritten partials
                     launch(&expand_mixed_kernel<DT, R, LP, SP, SplitSingle<DT, R>>, dim3((unsigned)xp.grid_expand),
                            dim3(kMixedThreads), st, (T*)y, (const T*)B_stack, seg_indptr,
                            adapter_ids, num_segments, num_rows, num_adapters, H2, scale,
                            (const float*)part, xp.two_sp, xp.two_sp.k[0], xp.two_sp.k[1],
-                           xp.two_sp.k[2]);
+                           xp.two_sp.k[2], (const int4*)items, n_items);
                 });
                 return launch_status();
             }

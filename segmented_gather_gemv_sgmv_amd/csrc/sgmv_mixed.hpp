@@ -820,15 +820,27 @@ __global__ __launch_bounds__(kMixedThreads, 4) void lora_mixed_kernel(
     }
 }
 
+// The expand launch's item table, written by the shrink launch of the same
+// call: entry q is expand item q (its tile and its column chunk: row0,
+// nrows, adapter, class | chunk << 2), and the int after the last of
+// n_max entries holds how many entries this call wrote.  Every entry below
+// that count is rewritten by each call, so the table needs no clearing.
+__device__ __forceinline__ int* item_count(int4* items, int n_max) {
+    return reinterpret_cast<int*>(items + n_max);
+}
+
 // The shrink half of the two-launch form: [long][short][single] shrink
 // items.  With v_final (sgmv_shrink), each tile's last item reduces the
 // partials into v (tile counters: long tiles, then short, then single).
+// With items, each tile's first item also writes the tile's expand items
+// (the expand launch then reads its item instead of scanning the table).
 template <typename DT, int R, typename LP, typename SP, typename GP>
 __global__ __launch_bounds__(kMixedThreads, R <= 32 ? 6 : (R == 64 ? 5 : 1)) void shrink_mixed_kernel(
     const typename DT::storage* __restrict__ x, const typename DT::storage* __restrict__ A_stack,
     const int* __restrict__ seg_indptr, const int* __restrict__ adapter_ids, int S, int num_rows,
     int num_adapters, int H1, float* __restrict__ partials, MixedSplit sp,
-    float* __restrict__ v_final, int* __restrict__ counters, int counter_stride) {
+    float* __restrict__ v_final, int* __restrict__ counters, int counter_stride,
+    int4* __restrict__ items, int n_items_max) {
     using C = MixedClasses<LP, SP, GP>;
     constexpr int NW = kMixedThreads / kWave;
     __shared__ __align__(16) unsigned char s_mem[C::kLdsBytes];
@@ -837,6 +849,9 @@ __global__ __launch_bounds__(kMixedThreads, R <= 32 ? 6 : (R == 64 ? 5 : 1)) voi
     MixedScan m;
     mixed_scan<C>(seg_indptr, adapter_ids, S, num_rows, num_adapters, s_scan, m);
     const int T0 = m.total[0], T1 = m.total[1], T2 = m.total[2];
+    const int E1 = T0 * sp.c[0], E2 = E1 + T1 * sp.c[1];  // first expand item of each class
+    if (items && blockIdx.x == 0 && threadIdx.x == 0)
+        *item_count(items, n_items_max) = min(E2 + T2 * sp.c[2], n_items_max);
     int q = (int)blockIdx.x, ti = 0, sub = 0, c;
     if (take_item(q, T0, sp.k[0], ti, sub)) c = 0;
     else if (take_item(q, T1, sp.k[1], ti, sub)) c = 1;
@@ -855,29 +870,55 @@ __global__ __launch_bounds__(kMixedThreads, R <= 32 ? 6 : (R == 64 ? 5 : 1)) voi
     else
         GP::shrink_split(t, sub, sp.h[2], sp.k[2], x, A_stack, H1, partials, row_stride, v_final,
                          cnt, &s_last, s_mem);
+    // after the stream, where its registers are free
+    if (items && sub == 0) {
+        const int per = sp.c[c];
+        const int base = (c == 0 ? 0 : (c == 1 ? E1 : E2)) + ti * per;
+        for (int s = (int)threadIdx.x; s < per; s += kMixedThreads)
+            if (base + s < n_items_max)
+                items[base + s] = make_int4(t.row0, t.nrows, t.adapter, c | (s << 2));
+    }
 }
 
 // The expand half: [long][short][single] expand items.  Rows of class c
-// have P[c] partials (sgmv_expand: 1, the partial is v).
+// have P[c] partials (sgmv_expand: 1, the partial is v).  With items (the
+// table the shrink launch of the same call wrote), a workgroup reads its
+// item there; else it scans the segment table.
 template <typename DT, int R, typename LP, typename SP, typename GP>
 __global__ __launch_bounds__(kMixedThreads, R >= 64 ? 4 : 5) void expand_mixed_kernel(
     typename DT::storage* __restrict__ y, const typename DT::storage* __restrict__ B_stack,
     const int* __restrict__ seg_indptr, const int* __restrict__ adapter_ids, int S, int num_rows,
     int num_adapters, int H2, float scale, const float* __restrict__ partials, MixedSplit sp,
-    int P_long, int P_short, int P_single) {
+    int P_long, int P_short, int P_single, const int4* __restrict__ items, int n_items_max) {
     using C = MixedClasses<LP, SP, GP>;
     constexpr int NW = kMixedThreads / kWave;
     __shared__ __align__(16) unsigned char s_mem[C::kLdsBytes];
     __shared__ int s_scan[kMixedScanInts];
-    MixedScan m;
-    mixed_scan<C>(seg_indptr, adapter_ids, S, num_rows, num_adapters, s_scan, m);
-    const int T0 = m.total[0], T1 = m.total[1], T2 = m.total[2];
-    int q = (int)blockIdx.x, ti = 0, sub = 0, c;
-    if (take_item(q, T0, sp.c[0], ti, sub)) c = 0;
-    else if (take_item(q, T1, sp.c[1], ti, sub)) c = 1;
-    else if (take_item(q, T2, sp.c[2], ti, sub)) c = 2;
-    else return;
-    const Tile t = mixed_find<C>(m, S, c, ti, s_scan);
+    Tile t;
+    int c, sub;
+    if (items) {
+        // both loads in flight together; the entry is in the table even
+        // for workgroups past the count (the grid is at most n_items_max)
+        const int n = *item_count(const_cast<int4*>(items), n_items_max);
+        const int4 e = items[blockIdx.x];
+        if ((int)blockIdx.x >= n) return;
+        t.row0 = e.x;
+        t.nrows = e.y;
+        t.adapter = e.z;
+        t.seg = -1;
+        c = e.w & 3;
+        sub = e.w >> 2;
+    } else {
+        MixedScan m;
+        mixed_scan<C>(seg_indptr, adapter_ids, S, num_rows, num_adapters, s_scan, m);
+        const int T0 = m.total[0], T1 = m.total[1], T2 = m.total[2];
+        int q = (int)blockIdx.x, ti = 0;
+        if (take_item(q, T0, sp.c[0], ti, sub)) c = 0;
+        else if (take_item(q, T1, sp.c[1], ti, sub)) c = 1;
+        else if (take_item(q, T2, sp.c[2], ti, sub)) c = 2;
+        else return;
+        t = mixed_find<C>(m, S, c, ti, s_scan);
+    }
     const long long row_stride = (long long)num_rows * R;
     if (c == 0)
         LP::expand_split(t, sub, y, B_stack, H2, scale, partials, row_stride, P_long, s_mem);

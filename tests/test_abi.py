@@ -105,7 +105,9 @@ def test_workspace_sizes(lib):
                                 (7, 3, 100, 90, 5, 1)]:
         n = lib.lora_apply_workspace_bytes(R, S, H1, H2, r, dt)
         counters = 256 * 1024  # fixed counter region at the front
-        assert n > counters and (n - counters) % (R * r * 4) == 0
+        # then float32 partials, whole [num_rows][r] chunks (and, for calls
+        # that take two launches, the expand launch's item table after them)
+        assert n >= counters + R * r * 4
         assert n == lib.lora_apply_workspace_bytes(R, S, H1, H2, r, dt)
         m = lib.sgmv_shrink_workspace_bytes(R, S, H1, r, dt)
         assert m == 0 or counters < m <= n

@@ -14,7 +14,7 @@ import pytest
 import oracle
 import workloads as wl
 from gpu_helpers import (assert_close, gpu_expand, gpu_lora_apply, gpu_shrink, magnitude,
-                         magnitude_expand, to_device, torch_dtype)
+                         magnitude_expand, to_device, torch_dtype, COUNTER_BYTES)
 
 pytestmark = pytest.mark.gpu
 
@@ -360,6 +360,51 @@ def test_graph_replay_matches_eager(which):
         torch.cuda.synchronize()
         assert torch.equal(y.double().cpu(), y_eager), f"replay {rep}"
         del junk
+
+
+def test_two_launch_graph_replay_with_changing_table():
+    """A call that takes two launches, captured in a HIP graph and replayed
+    while the segment table's contents change between replays (its size
+    fixed): each replay's expand launch takes exactly the items its own
+    shrink launch listed, never the longer list an earlier replay left."""
+    import torch
+    import segmented_gather_gemv_sgmv_amd as sg
+    R, H1, H2, r, N = 2000, 512, 1024, 128, 6
+    tables = {
+        "full": [300, 180, 250, 170, 200, 160, 140, 120, 130, 110, 120, 120],
+        "small": [1, 0, 3, 17, 0, 1, 40, 2, 0, 9, 1, 5],
+        "mid": [600, 0, 1, 1, 7, 300, 0, 15, 16, 2, 400, 3],
+    }
+    S = len(tables["full"])
+    ids = [3, 0, 5, 1, 4, 2, 5, 0, 1, 3, 2, 4]
+    ws_of = {k: wl.make_workload(k, "f16", H1, H2, r, N, v, ids, 1.25, seed=78, num_rows=R)
+             for k, v in tables.items()}
+    w = ws_of["full"]
+    need = sg.lora_apply_workspace_bytes(R, S, H1, H2, r, torch.float16)
+    # the item table after the partials: this shape takes two launches
+    assert (need - COUNTER_BYTES) % (R * r * 4) != 0
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    d = to_device(w)
+    y = d["y0"].clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        sg.lora_apply(y, d["x"], d["A"], d["B"], d["seg"], d["ids"], w.scale, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sg.lora_apply(y, d["x"], d["A"], d["B"], d["seg"], d["ids"], w.scale, workspace=ws)
+    for name in ["full", "small", "full", "mid", "small", "mid"]:
+        wk = ws_of[name]
+        d["seg"].copy_(torch.from_numpy(wk.seg_indptr.astype(np.int32)))
+        y.copy_(d["y0"])
+        g.replay()
+        torch.cuda.synchronize()
+        y_ref, _ = oracle.lora_apply(wk.y0, wk.x, wk.A, wk.B, wk.seg_indptr, wk.adapter_ids,
+                                     wk.scale)
+        assert_close(y.double().cpu().numpy(), y_ref, "f16", f"replay on {name}")
+        assert int(ws[:COUNTER_BYTES].view(torch.int32).abs().sum()) == 0
 
 
 def test_capture_without_workspace_is_refused():
