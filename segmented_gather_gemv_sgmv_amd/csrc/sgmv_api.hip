@@ -117,6 +117,13 @@ constexpr int kCounterStride = 32;
 constexpr int kCounterSlots = kCounterInts / kCounterStride - 1;
 constexpr size_t kCounterBytes = kCounterInts * sizeof(int);
 
+// Columns of an MFMA expand item (MfmaShape::kCW in sgmv_mfma.hpp).
+constexpr int mfma_expand_cols(int r) { return r >= 64 ? 256 : std::min(512, 8192 / r); }
+static_assert(mfma_expand_cols(16) == MfmaShape<16>::kCW && mfma_expand_cols(32) == MfmaShape<32>::kCW &&
+                  mfma_expand_cols(64) == MfmaShape<64>::kCW &&
+                  mfma_expand_cols(128) == MfmaShape<128>::kCW,
+              "host and device agree on the expand item width");
+
 // Launch plan of the single-kernel lora_apply (a pure function of shapes).
 struct FusedPlan {
     bool ok;            // shapes allow it (alignment is checked per call)
@@ -194,7 +201,7 @@ MfmaPlan make_mfma_plan(int num_rows, int num_segments, int H1, int H2, int r, i
     }
     const long long slots = f.slots_a + f.slots_b;
     const int kc_max = 16384 / r;
-    const int cw = (8192 / r) < 512 ? (8192 / r) : 512;
+    const int cw = mfma_expand_cols(r);
     f.csplit = (H2 + cw - 1) / cw;
     // Fewest chunks that fit the LDS copy of A, more while items still fit
     // one resident wave and chunks keep at least 256 rows of A.
@@ -230,7 +237,7 @@ MfmaSplitPlan make_mfma_split_plan(const MfmaPlan& mp, int H1, int H2, int r) {
     sp.slots = mp.slots_a + mp.slots_b;
     if (sp.slots * (mp.ksplit + mp.csplit) <= 2LL * kFusedItems) return sp;
     const int kc_max = 16384 / r;
-    const int cw = (8192 / r) < 512 ? (8192 / r) : 512;
+    const int cw = mfma_expand_cols(r);
     sp.csplit = (H2 + cw - 1) / cw;
     // Fewest chunks that fit the LDS copy of A, more while the shrink launch
     // has fewer than kTargetWorkgroups workgroups and chunks keep >= 256 rows.
@@ -290,7 +297,7 @@ MixedShape mixed_shape(int H1, int H2, int r, int dtype) {
     m.TH = !m.has_long ? 0x7FFFFFFF : (m.has_short ? 16 : 2);
     const int vunit = kMixedThreads / (r / vec);
     m.T[0] = 16;
-    m.cw[0] = std::min(512, 8192 / r);
+    m.cw[0] = mfma_expand_cols(r);
     m.unit[0] = 128;
     m.hmax[0] = std::max(128, 8192 / r);  // MfmaTile's LDS chunk of A
     m.T[1] = 4;

@@ -111,9 +111,16 @@ struct MfmaShape {
     static constexpr int kKcMax = KC;                    // rows of A per LDS chunk (default 32 KB)
     static_assert(KC % (32 * kNW) == 0, "a chunk is whole K steps of every wave");
     static constexpr int kXSteps = kKcMax / (32 * kNW);  // K steps of 32 per wave and chunk
-    static constexpr int kCW = (8192 / R) < 512 ? (8192 / R) : 512;  // expand columns per item
+    // Expand columns per item.  Up to rank 32 the item's whole B chunk
+    // (R x kCW) sits in LDS at once; from rank 64 it passes through LDS in
+    // slices of kKS = 32 ranks, the next slice loading into registers while
+    // the current one is multiplied, so the item keeps 256 columns (a
+    // slice then takes the LDS the tile's A chunk takes).
+    static constexpr int kCW = R >= 64 ? 256 : ((8192 / R) < 512 ? (8192 / R) : 512);
+    static constexpr int kKS = R >= 64 ? 32 : R;         // ranks of B per LDS stage
+    static constexpr int kSlices = R / kKS;
     static constexpr int kCBW = kCW / (16 * kNW);        // 16-column blocks per wave
-    static constexpr int kBV = R * kCW / 8 / kNT;        // 16-byte B vectors per thread
+    static constexpr int kBV = kKS * kCW / 8 / kNT;      // 16-byte B vectors per thread and slice
     // Epilogue: y is read and written in row-contiguous 16-byte pieces (kYU
     // pieces of 8 columns per thread; a wave covers 512 columns of a row),
     // and the 16 x kCW tile of y passes through LDS (over the B chunk, which
@@ -121,17 +128,18 @@ struct MfmaShape {
     // 8-byte group g of row i sits at position g ^ (i & 15), so that neither
     // the row-piece accesses nor the MFMA-layout ones meet bank conflicts.
     static constexpr int kYU = (2 * kCW + kNT - 1) / kNT;
-    // The B chunk in LDS: R rows of kCW columns, each row padded by 16
+    // A B slice in LDS: kKS rows of kCW columns, each row padded by 16
     // elements so that the four rows one transposing read touches fall in
     // different banks.
     static constexpr int kLdB = kCW + 16;
-    static constexpr int kStageB = R * kLdB;  // LDS of the B chunk, in 16-bit units
+    static constexpr int kStageB = kKS * kLdB;  // LDS of a B slice, in 16-bit units
     // K of the expand's v operand: three 16-bit terms of each v, padded to
     // whole MFMA steps of 32 (16-bit units per tile row of s_vh).
     static constexpr int kVK = (3 * R + 31) / 32 * 32;
     static_assert(kStageB >= kT * kCW, "the y tile must fit over the B chunk");
     static_assert(kCW % 64 == 0, "the swizzle needs at least 16 groups per row");
-    static_assert(kBV * kNT * 8 == R * kCW, "B chunk must split evenly over the threads");
+    static_assert(kBV * kNT * 8 == kKS * kCW, "a B slice must split evenly over the threads");
+    static_assert(kSlices == 1 || 3 * R == kVK, "sliced ranks need no K padding");
     static_assert(R % 16 == 0 && R <= 128, "MFMA path needs r in {16, 32, 64, 128}");
 };
 
@@ -325,13 +333,31 @@ __device__ __forceinline__ void shrink_long_mfma(const typename DT::storage* __r
 }
 
 // The part of an expand item (tile rows x columns [c0, c0 + kCW)) that does
-// not depend on v, loaded first: this thread's 16-byte pieces of the B chunk
-// and the y values its lane updates.
+// not depend on v, loaded first: this thread's 16-byte pieces of the first
+// B slice and the y values its lane updates.
 template <int R>
 struct ExpandRegs {
     uint4 bq[MfmaShape<R>::kBV];
     uint4 yv[MfmaShape<R>::kYU];  // piece u: row u / (kCW / 8), columns 8 (u % (kCW / 8)) + [0, 8)
 };
+
+// This thread's pieces of B slice sl (ranks sl * kKS + [0, kKS)).
+template <typename DT, int R>
+__device__ __forceinline__ void expand_load_slice(uint4 (&bq)[MfmaShape<R>::kBV],
+                                                  const typename DT::storage* __restrict__ B,
+                                                  int sl, int H2, int c0) {
+    using Sh = MfmaShape<R>;
+    constexpr int CW = Sh::kCW;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < Sh::kBV; ++u) {
+        const int t = tid + u * Sh::kNT;
+        const int kr = sl * Sh::kKS + t / (CW / 8);
+        const int c8 = (t % (CW / 8)) * 8;
+        bq[u] = (c0 + c8 < H2) ? load16(B + (long long)kr * H2 + c0 + c8)
+                               : make_uint4(0, 0, 0, 0);
+    }
+}
 
 template <typename DT, int R>
 __device__ __forceinline__ void expand_prefetch(ExpandRegs<R>& e,
@@ -341,14 +367,7 @@ __device__ __forceinline__ void expand_prefetch(ExpandRegs<R>& e,
     using Sh = MfmaShape<R>;
     constexpr int CW = Sh::kCW;
     const int tid = threadIdx.x;
-#pragma unroll
-    for (int u = 0; u < Sh::kBV; ++u) {
-        const int t = tid + u * Sh::kNT;
-        const int kr = t / (CW / 8);
-        const int c8 = (t % (CW / 8)) * 8;
-        e.bq[u] = (c0 + c8 < H2) ? load16(B + (long long)kr * H2 + c0 + c8)
-                                 : make_uint4(0, 0, 0, 0);
-    }
+    expand_load_slice<DT, R>(e.bq, B, 0, H2, c0);
 #pragma unroll
     for (int j = 0; j < Sh::kYU; ++j) {
         const int u = tid + j * Sh::kNT;
@@ -370,23 +389,31 @@ template <typename DT, int R>
 __device__ __forceinline__ void expand_apply(const ExpandRegs<R>& e, uint16_t* s_b,
                                              const float* s_v, uint16_t* s_vh, float* s_max,
                                              typename DT::storage* __restrict__ yr, int nrows,
-                                             int H2, int c0, float scale) {
+                                             int H2, int c0, float scale,
+                                             const typename DT::storage* __restrict__ B) {
     using Sh = MfmaShape<R>;
     using Ops = MfmaOps<DT>;
     constexpr int T = Sh::kT;
     constexpr int NT = Sh::kNT;
     constexpr int CW = Sh::kCW;
     constexpr int CBW = Sh::kCBW;
+    constexpr int NS = Sh::kSlices;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wid = tid / kWave;
     const int m = lane & 15;
     const int grp = lane >> 4;
+    uint4 bq[Sh::kBV];
 #pragma unroll
-    for (int u = 0; u < Sh::kBV; ++u) {
-        const int t = tid + u * NT;
-        store16(s_b + (t / (CW / 8)) * Sh::kLdB + (t % (CW / 8)) * 8, e.bq[u]);
-    }
+    for (int u = 0; u < Sh::kBV; ++u) bq[u] = e.bq[u];
+    auto stage = [&]() {  // this thread's pieces of the slice in bq -> s_b
+#pragma unroll
+        for (int u = 0; u < Sh::kBV; ++u) {
+            const int t = tid + u * NT;
+            store16(s_b + (t / (CW / 8)) * Sh::kLdB + (t % (CW / 8)) * 8, bq[u]);
+        }
+    };
+    stage();
     // The largest |v| of the tile for the fp16 range scaling.
     int shift = 0;
     if constexpr (Ops::kScaleV) {
@@ -427,17 +454,45 @@ __device__ __forceinline__ void expand_apply(const ExpandRegs<R>& e, uint16_t* s
     const float out_scale = ldexpf(scale, -shift);
     mf32x4 acc[CBW];
 #pragma unroll
-    for (int q = 0; q < CBW; ++q) {
-        const int cb = wid * CBW + q;
-        acc[q] = mf32x4{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < CBW; ++q) acc[q] = mf32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (NS == 1) {
 #pragma unroll
-        for (int ks = 0; ks < VK / 32; ++ks) {
-            // B rows kr .. kr + 7 (every term of v meets B row kr), columns
-            // cb * 16 + [0, 16).
-            const int kr = (ks * 32 + grp * 8) % R;
-            const uint4 ab = lds_operand_tr(s_b + cb * 16, kr, Sh::kLdB, m);
-            const uint4 bv = *reinterpret_cast<const uint4*>(s_vh + m * VK + ks * 32 + grp * 8);
-            acc[q] = Ops::mma(ab, bv, acc[q]);
+        for (int q = 0; q < CBW; ++q) {
+            const int cb = wid * CBW + q;
+#pragma unroll
+            for (int ks = 0; ks < VK / 32; ++ks) {
+                // B rows kr .. kr + 7 (every term of v meets B row kr), columns
+                // cb * 16 + [0, 16).
+                const int kr = (ks * 32 + grp * 8) % R;
+                const uint4 ab = lds_operand_tr(s_b + cb * 16, kr, Sh::kLdB, m);
+                const uint4 bv =
+                    *reinterpret_cast<const uint4*>(s_vh + m * VK + ks * 32 + grp * 8);
+                acc[q] = Ops::mma(ab, bv, acc[q]);
+            }
+        }
+    } else {
+        // Slice sl holds B rows sl * 32 + [0, 32); each of the three terms
+        // of v meets them in one K step.  The next slice is in flight while
+        // this one is multiplied.
+        expand_load_slice<DT, R>(bq, B, 1, H2, c0);
+        for (int sl = 0; sl < NS; ++sl) {
+            if (sl > 0) {
+                __syncthreads();  // every wave is done with slice sl - 1
+                stage();
+                __syncthreads();
+                if (sl + 1 < NS) expand_load_slice<DT, R>(bq, B, sl + 1, H2, c0);
+            }
+#pragma unroll
+            for (int q = 0; q < CBW; ++q) {
+                const int cb = wid * CBW + q;
+                const uint4 ab = lds_operand_tr(s_b + cb * 16, grp * 8, Sh::kLdB, m);
+#pragma unroll
+                for (int term = 0; term < 3; ++term) {
+                    const uint4 bv = *reinterpret_cast<const uint4*>(
+                        s_vh + m * VK + term * R + sl * Sh::kKS + grp * 8);
+                    acc[q] = Ops::mma(ab, bv, acc[q]);
+                }
+            }
         }
     }
     // The y tile, as loaded (row pieces), into LDS over the B chunk: every
@@ -580,7 +635,7 @@ __global__ __launch_bounds__(256) void lora_mfma_kernel(
     int before = 0;
     if (tid == 0) before = depart_begin(cnt, 1 << 16);
     expand_apply<DT, R>(er, s_a, s_v, s_vh, s_max, y + (long long)tile.row0 * H2, nrows, H2, c0,
-                        scale);
+                        scale, B_stack + (long long)tile.adapter * R * H2);
     if (tid == 0) depart_end(cnt, before, 1 << 16, total);
 }
 
@@ -718,7 +773,7 @@ __global__ __launch_bounds__(256) void expand_mfma_kernel(
     }
     __syncthreads();
     expand_apply<DT, R>(er, s_b, s_v, s_vh, s_max, y + (long long)tile.row0 * H2, nrows, H2, c0,
-                        scale);
+                        scale, B_stack + (long long)tile.adapter * R * H2);
 }
 
 }  // namespace sgmv

@@ -431,7 +431,8 @@ struct MfmaTile {
         __syncthreads();
         int before = 0;
         if (tid == 0) before = depart_begin(cnt, 1 << 16);
-        expand_apply<DT, R>(er, s_a(lds), sv, s_vh(lds), s_max(lds), yr, t.nrows, H2, c0, scale);
+        expand_apply<DT, R>(er, s_a(lds), sv, s_vh(lds), s_max(lds), yr, t.nrows, H2, c0, scale,
+                            B);
         if (tid == 0) depart_end(cnt, before, 1 << 16, total);
     }
 
@@ -469,7 +470,8 @@ struct MfmaTile {
                                 : 0.f;
         }
         __syncthreads();
-        expand_apply<DT, R>(er, s_a(lds), sv, s_vh(lds), s_max(lds), yr, t.nrows, H2, c0, scale);
+        expand_apply<DT, R>(er, s_a(lds), sv, s_vh(lds), s_max(lds), yr, t.nrows, H2, c0, scale,
+                            B_stack + (long long)t.adapter * R * H2);
     }
 };
 

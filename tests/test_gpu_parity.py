@@ -369,7 +369,7 @@ def test_two_launch_graph_replay_with_changing_table():
     shrink launch listed, never the longer list an earlier replay left."""
     import torch
     import segmented_gather_gemv_sgmv_amd as sg
-    R, H1, H2, r, N = 2000, 512, 1024, 128, 6
+    R, H1, H2, r, N = 2000, 512, 4096, 128, 6  # rank 128: B passes through LDS in slices
     tables = {
         "full": [300, 180, 250, 170, 200, 160, 140, 120, 130, 110, 120, 120],
         "small": [1, 0, 3, 17, 0, 1, 40, 2, 0, 9, 1, 5],
@@ -565,7 +565,7 @@ def test_shrink_in_kernel_reduction_is_deterministic():
 
 @pytest.mark.parametrize("seed,dtype,H1,H2,r,N,R,S,tail", [
     (41, "bf16", 1024, 3072, 64, 7, 3000, 5, 0),
-    (42, "f16", 512, 1024, 128, 4, 2000, 3, 37),
+    (42, "f16", 512, 3000, 128, 4, 2000, 3, 37),  # ragged last column chunk
     # more than two rounds of one-chunk workgroups: each shrink workgroup
     # sums several LDS-sized chunks (ragged last range)
     (43, "f16", 2048, 1024, 128, 6, 2400, 4, 19),
@@ -575,7 +575,10 @@ def test_two_launch_mfma_path(seed, dtype, H1, H2, r, N, R, S, tail):
     """Row-heavy calls too large for one resident round of single-kernel
     items run as a shrink launch and an expand launch; ragged segments
     (some empty) and rows outside every segment included."""
+    import segmented_gather_gemv_sgmv_amd as sg
     w = wl.small_random(seed, dtype, H1, H2, r, N, R, S, uncovered_tail=tail)
+    need = sg.lora_apply_workspace_bytes(R, S, H1, H2, r, torch_dtype(dtype))
+    assert (need - COUNTER_BYTES) % (R * r * 4) != 0, "the expand item table: two launches"
     y_ref, _ = oracle.lora_apply(w.y0, w.x, w.A, w.B, w.seg_indptr, w.adapter_ids, w.scale)
     y = gpu_lora_apply(w)
     assert_close(y, y_ref, dtype, w.name)
