@@ -368,6 +368,26 @@ def rows_sweep(steps: int, warmup: int, rows=SWEEP_ROWS):
         yield out
 
 
+def ranks_sweep(steps: int, warmup: int, ranks=(16, 32, 64, 128), dtypes=("f16", "bf16")):
+    """The prefill shape (4096 rows, 4096 -> 4096, the same 16 segments and
+    adapters) at every rank the MFMA path serves, in fp16 and bf16: lora_apply
+    per call, cold, against its algorithmic bytes.  Yields one dict per
+    (dtype, rank)."""
+    import numpy as np
+    import workloads as wl
+    lengths = [int(n) for n in np.diff(wl.prefill(seed=0).seg_indptr)]
+    for dtype in dtypes:
+        for r in ranks:
+            w = wl.make_workload(f"prefill_4096_r{r}_{dtype}", dtype, 4096, 4096, r, 16, lengths,
+                                 list(range(16)), 2.0, seed=1)
+            res = run_gpu(w, steps, warmup, replays=3)
+            us = res["gpu_ms"] * 1e3 / steps
+            gbps = algorithmic_bytes(w) / us / 1e3
+            yield {"dtype": dtype, "r": r, "us": us, "algorithmic_bytes": algorithmic_bytes(w),
+                   "achieved_hbm_GBps": gbps, "frac_of_8TBps": gbps / 8000.0,
+                   "fallback_flag": res["fallback_flag"]}
+
+
 def copy_floor(w, steps: int, warmup: int, device="cuda:0", nbytes=None):
     """What a plain device-to-device copy moving the workload's algorithmic
     bytes per call (half read, half written) costs under the same method:
@@ -597,6 +617,8 @@ def main(argv=None):
     ap.add_argument("--sweep", action="store_true",
                     help="instead: latency against rows per call (1..256) at the decode shape, "
                          "distinct and identical adapters, beside the base layer's GEMM")
+    ap.add_argument("--ranks", action="store_true",
+                    help="instead: the prefill shape at ranks 16, 32, 64 and 128, fp16 and bf16")
     ap.add_argument("--linear", choices=("fused", "unfused", "base"), default=None,
                     help="instead: time the adapted linear layer over the workload's batch, "
                          "base product fused in (lora_linear) or not (addmm + lora_apply)")
@@ -638,6 +660,10 @@ def main(argv=None):
         return 0
     if args.sweep:
         for point in rows_sweep(min(args.steps, 400), min(args.warmup, 40)):
+            print(json.dumps(point), flush=True)
+        return 0
+    if args.ranks:
+        for point in ranks_sweep(min(args.steps, 200), min(args.warmup, 20)):
             print(json.dumps(point), flush=True)
         return 0
     P = args.projections
