@@ -368,24 +368,29 @@ def rows_sweep(steps: int, warmup: int, rows=SWEEP_ROWS):
         yield out
 
 
-def ranks_sweep(steps: int, warmup: int, ranks=(16, 32, 64, 128), dtypes=("f16", "bf16")):
-    """The prefill shape (4096 rows, 4096 -> 4096, the same 16 segments and
-    adapters) at every rank the MFMA path serves, in fp16 and bf16: lora_apply
-    per call, cold, against its algorithmic bytes.  Yields one dict per
-    (dtype, rank)."""
+def ranks_sweep(steps: int, warmup: int):
+    """lora_apply across ranks, cold, against its algorithmic bytes: the
+    prefill shape (4096 rows, 4096 -> 4096, the same 16 segments and
+    adapters) at ranks 16..128 in fp16 and bf16 (the ranks the matrix cores
+    serve), and the decode shape (64 rows, each its own adapter) at ranks
+    8..128 in fp16, bf16 and fp32.  Yields one dict per (shape, dtype, rank)."""
     import numpy as np
     import workloads as wl
     lengths = [int(n) for n in np.diff(wl.prefill(seed=0).seg_indptr)]
-    for dtype in dtypes:
-        for r in ranks:
+    cases = [("prefill", d, r) for d in ("f16", "bf16") for r in (16, 32, 64, 128)]
+    cases += [("decode", d, r) for d in ("f16", "bf16", "f32") for r in (8, 16, 32, 64, 128)]
+    for shape, dtype, r in cases:
+        if shape == "prefill":
             w = wl.make_workload(f"prefill_4096_r{r}_{dtype}", dtype, 4096, 4096, r, 16, lengths,
                                  list(range(16)), 2.0, seed=1)
-            res = run_gpu(w, steps, warmup, replays=3)
-            us = res["gpu_ms"] * 1e3 / steps
-            gbps = algorithmic_bytes(w) / us / 1e3
-            yield {"dtype": dtype, "r": r, "us": us, "algorithmic_bytes": algorithmic_bytes(w),
-                   "achieved_hbm_GBps": gbps, "frac_of_8TBps": gbps / 8000.0,
-                   "fallback_flag": res["fallback_flag"]}
+        else:
+            w = wl.decode_batch(64, distinct=True, r=r, dtype=dtype, num_adapters=64)
+        res = run_gpu(w, steps, warmup, replays=3)
+        us = res["gpu_ms"] * 1e3 / steps
+        gbps = algorithmic_bytes(w) / us / 1e3
+        yield {"shape": shape, "dtype": dtype, "r": r, "us": us,
+               "algorithmic_bytes": algorithmic_bytes(w), "achieved_hbm_GBps": gbps,
+               "frac_of_8TBps": gbps / 8000.0, "fallback_flag": res["fallback_flag"]}
 
 
 def copy_floor(w, steps: int, warmup: int, device="cuda:0", nbytes=None):
@@ -618,7 +623,8 @@ def main(argv=None):
                     help="instead: latency against rows per call (1..256) at the decode shape, "
                          "distinct and identical adapters, beside the base layer's GEMM")
     ap.add_argument("--ranks", action="store_true",
-                    help="instead: the prefill shape at ranks 16, 32, 64 and 128, fp16 and bf16")
+                    help="instead: the prefill shape at ranks 16..128 (fp16, bf16) and the decode "
+                         "shape at ranks 8..128 (fp16, bf16, fp32)")
     ap.add_argument("--linear", choices=("fused", "unfused", "base"), default=None,
                     help="instead: time the adapted linear layer over the workload's batch, "
                          "base product fused in (lora_linear) or not (addmm + lora_apply)")

@@ -303,7 +303,7 @@ MixedShape mixed_shape(int H1, int H2, int r, int dtype) {
     m.T[1] = 4;
     m.T[2] = 1;
     for (int c = 1; c < 3; ++c) {
-        m.cw[c] = kMixedThreads * vec;
+        m.cw[c] = kMixedThreads * vec / vec_rank_groups(r, m.T[c]);  // VecTile::kCW
         m.unit[c] = vunit;
         m.hmax[c] = 0;
     }

@@ -93,7 +93,13 @@ __device__ __forceinline__ void reduce_if_last(const Tile& t, int ksplit, float*
 // items stream kCW columns of B and y, one 16-byte piece per thread and row,
 // KB rows of B in flight per thread.
 // ---------------------------------------------------------------------------
-template <typename DT, int R, int RB, int KB = (R < 16 ? R : 16)>
+// Rank groups of a one-row expand item: from rank 32 an item's threads split
+// its ranks into R / 16 groups, each streaming its ranks of B for fewer
+// columns, so that an item moves about 64 KB of B whatever the rank (one
+// CU streams a few hundred KB far slower than the chip's rate).
+constexpr int vec_rank_groups(int R, int RB) { return RB == 1 && R >= 32 ? R / 16 : 1; }
+
+template <typename DT, int R, int RB, int KB = (R < 16 ? R : 16), int KG = vec_rank_groups(R, RB)>
 struct VecTile {
     using st = typename DT::storage;
     static constexpr int NT = kMixedThreads;
@@ -103,14 +109,29 @@ struct VecTile {
     static constexpr int NW = NT / kWave;
     static constexpr int N = RB * kVec;
     static constexpr int kPG = 4;
-    static constexpr int kKB = KB;  // rows of B in flight per thread
-    static constexpr int kCW = NT * kVec;    // expand columns per item
+    static constexpr int kGT = NT / KG;              // threads of a rank group
+    static constexpr int kRG = R / KG;               // ranks of a group
+    static constexpr int kKB = KB < kRG ? KB : kRG;  // rows of B in flight per thread
+    static constexpr int kCW = kGT * kVec;           // expand columns per item
     static constexpr int kHUnit = NT / LPR;  // rows of A per block-wide pass
     static constexpr int kHMax = 0;          // a chunk may be any length
     static constexpr int kRedFloats = NW * LPR * N;
-    // LDS: s_red [kRedFloats] | s_v [RB * R] | flag
-    static constexpr int kLdsBytes = (kRedFloats + RB * R) * 4 + 16;
+    // LDS: s_red [kRedFloats] | s_v [RB * R] | flag | the groups' sums [KG - 1][kCW]
+    static constexpr int kLdsBytes = (kRedFloats + RB * R) * 4 + 16 + (KG - 1) * kCW * 4;
     static_assert(R % kVec == 0 && kWave % LPR == 0, "vector rank");
+    static_assert(KG == 1 || RB == 1, "rank groups for one-row tiles");
+    static_assert(R % KG == 0 && NT % KG == 0 && kRG % kKB == 0, "even rank groups");
+
+    // This thread's rank group and its first column in column chunk c.
+    __device__ static __forceinline__ int group() { return (int)threadIdx.x / kGT; }
+    __device__ static __forceinline__ int col(int c) {
+        return c * kCW + ((int)threadIdx.x % kGT) * kVec;
+    }
+    // This thread's pieces of B: its group's ranks, from column j.
+    __device__ static __forceinline__ const st* b_ptr(const st* __restrict__ B_stack, int adapter,
+                                                      int H2, int j) {
+        return B_stack + (long long)adapter * R * H2 + (long long)group() * kRG * H2 + j;
+    }
 
     __device__ static __forceinline__ float* s_v(unsigned char* lds) {
         return reinterpret_cast<float*>(lds) + kRedFloats;
@@ -161,8 +182,10 @@ struct VecTile {
         for (int i = 0; i < RB; ++i)
 #pragma unroll
             for (int q = 0; q < kVec; ++q) acc[i][q] = 0.f;
+        const int g = group();
+        const float* sv = s_v + g * kRG;  // this group's ranks
 #pragma unroll
-        for (int kb = 0; kb < R; kb += kKB) {
+        for (int kb = 0; kb < kRG; kb += kKB) {
             if (kb > 0) {
 #pragma unroll
                 for (int kk = 0; kk < kKB; ++kk)
@@ -175,12 +198,27 @@ struct VecTile {
 #pragma unroll
                 for (int i = 0; i < RB; ++i) {
                     if (i < t.nrows) {
-                        const float vv = s_v[i * R + kb + kk];
+                        const float vv = sv[i * R + kb + kk];
 #pragma unroll
                         for (int q = 0; q < kVec; ++q) acc[i][q] = fmaf(vv, bf[q], acc[i][q]);
                     }
                 }
             }
+        }
+        if constexpr (KG > 1) {
+            // groups 1.. leave their sums; group 0 adds them in group order
+            float* s_part = const_cast<float*>(s_v) + RB * R + 4;
+            const int jp = (int)threadIdx.x % kGT;
+            if (g > 0) {
+#pragma unroll
+                for (int q = 0; q < kVec; ++q) s_part[(g - 1) * kCW + jp * kVec + q] = acc[0][q];
+            }
+            __syncthreads();
+            if (g > 0) return;
+#pragma unroll
+            for (int gg = 1; gg < KG; ++gg)
+#pragma unroll
+                for (int q = 0; q < kVec; ++q) acc[0][q] += s_part[(gg - 1) * kCW + jp * kVec + q];
         }
         if (!active) return;
 #pragma unroll
@@ -202,9 +240,10 @@ struct VecTile {
 #pragma unroll
         for (int kk = 0; kk < kKB; ++kk)
             bv[kk] = active ? load16(Bj + (long long)kk * H2) : make_uint4(0, 0, 0, 0);
+        const bool first = group() == 0;  // only group 0 updates y
 #pragma unroll
         for (int i = 0; i < RB; ++i)
-            yv[i] = (active && i < t.nrows)
+            yv[i] = (active && first && i < t.nrows)
                         ? load16_stream(y + (long long)(t.row0 + i) * H2 + j)
                         : make_uint4(0, 0, 0, 0);
     }
@@ -220,9 +259,9 @@ struct VecTile {
         float* s_v = reinterpret_cast<float*>(lds) + kRedFloats;
         int* s_flag = reinterpret_cast<int*>(s_v + RB * R);
         const int tid = threadIdx.x;
-        const int j = c * kCW + tid * kVec;
+        const int j = col(c);
         const bool active = j < H2;
-        const st* Bj = B_stack + (long long)t.adapter * R * H2 + j;
+        const st* Bj = b_ptr(B_stack, t.adapter, H2, j);
         uint4 bv[kKB];
         uint4 yv[RB];
         expand_loads(bv, yv, Bj, y, t, j, active, H2);
@@ -283,9 +322,9 @@ struct VecTile {
                                                         unsigned char* lds) {
         float* s_v = reinterpret_cast<float*>(lds) + kRedFloats;
         const int tid = threadIdx.x;
-        const int j = c * kCW + tid * kVec;
+        const int j = col(c);
         const bool active = j < H2;
-        const st* Bj = B_stack + (long long)t.adapter * R * H2 + j;
+        const st* Bj = b_ptr(B_stack, t.adapter, H2, j);
         uint4 bv[kKB];
         uint4 yv[RB];
         expand_loads(bv, yv, Bj, y, t, j, active, H2);
