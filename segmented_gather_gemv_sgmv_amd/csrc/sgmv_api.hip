@@ -293,7 +293,7 @@ MixedShape mixed_shape(int H1, int H2, int r, int dtype) {
     m.e = elem_bytes(dtype);
     m.r = r;
     m.has_long = mfma_rank;
-    m.has_short = !mfma_rank || r >= 64;
+    m.has_short = !mfma_rank;
     m.TH = !m.has_long ? 0x7FFFFFFF : (m.has_short ? 16 : 2);
     const int vunit = kMixedThreads / (r / vec);
     m.T[0] = 16;
@@ -469,9 +469,7 @@ void with_mixed(int dtype, int r, F&& f) {
         auto go = [&](auto rank) {
             constexpr int R = decltype(rank)::value;
             using G = VecTile<DT, R, 1>;
-            if constexpr (!std::is_same<DT, F32>::value && R >= 64)
-                f(dt, rank, MfmaTile<DT, R>{}, ShortTile<DT, R>{}, G{});
-            else if constexpr (!std::is_same<DT, F32>::value && R >= 16)
+            if constexpr (!std::is_same<DT, F32>::value && R >= 16)
                 f(dt, rank, MfmaTile<DT, R>{}, NoTile<DT>{}, G{});
             else
                 f(dt, rank, NoTile<DT>{}, ShortTile<DT, R>{}, G{});

@@ -16,10 +16,11 @@
 //   short  (2 <= n < TH rows)   tiles of 4 rows on the vector units
 //   single (n == 1)             one-row tiles on the vector units (GEMV)
 //
-// TH is 2 at ranks 16 and 32, where the MFMA expand tile is wide enough to
-// pay for itself on a few rows (no short class), 16 at ranks 64 and 128,
-// whose MFMA expand tile is narrow (its B chunk must fit LDS), and infinite
-// where the matrix cores do not apply (float32, rank 8: no long class).
+// TH is 2 wherever the matrix cores apply (fp16 and bf16 at ranks 16 to
+// 128): a 16-row MFMA tile pays for itself from two rows, since it reads its
+// adapter once however few rows it holds and its expand items are at least
+// 256 columns wide (there is no short class).  TH is infinite where they do
+// not apply (float32, rank 8: no long class; the short class serves 2..n).
 // All classes run in the same launch.  Every workgroup scans the segment
 // table once (up to kMixedMaxSegments entries, all loads in flight
 // together), which gives it the number of tiles of each class and the place

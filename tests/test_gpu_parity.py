@@ -285,15 +285,15 @@ def test_single_segment_guess_holds_or_falls_back(kind, dtype, r, R):
 def test_guessed_tables_across_dtypes_and_ranks(shape, dtype, r, H):
     """Both guessed table shapes (one row per segment; one segment over every
     row) on every class a dtype and rank can put them in: one-row vector
-    tiles, 4-row vector tiles (float32, rank 8, ranks >= 64 below 16 rows),
-    MFMA tiles."""
+    tiles, 4-row vector tiles (float32, rank 8), MFMA tiles (fp16 and bf16
+    from rank 16, one partial tile at 13 rows)."""
     N = 6
     rng = np.random.default_rng(zlib.crc32(f"{shape}{dtype}{r}{H}".encode()))
     if shape == "rows_eq_segments":
         R = 40
         lengths, ids = np.ones(R, np.int64), rng.integers(0, N, size=R).astype(np.int32)
     else:
-        R = 37 if r < 64 else 13  # ragged last tile; at r >= 64 below the MFMA threshold
+        R = 37 if r < 64 else 13  # a ragged last tile; at r >= 64 a single partial one
         lengths, ids = [R], [int(rng.integers(0, N))]
     w = wl.make_workload(f"guess_{shape}", dtype, H, H, r, N, lengths, ids, 0.75, rng=rng)
     y_ref, _ = oracle.lora_apply(w.y0, w.x, w.A, w.B, w.seg_indptr, w.adapter_ids, w.scale)
