@@ -409,6 +409,8 @@ MixedSplit mixed_split(const MixedShape& ms, int R, int S, int H1, int H2, bool 
     return sp;
 }
 
+constexpr long long kSelfMaxA = 32768;  // bytes of one adapter's A (see make_mixed_plan)
+
 struct MixedPlan {
     bool ok;
     bool two;              // two launches (else one)
@@ -428,6 +430,16 @@ MixedPlan make_mixed_plan(const MixedShape& ms, int R, int S, int H1, int H2) {
     const long long ones[3] = {1, 1, 1};
     p.tiles = mixed_bound(R, S, ms, ones);
     p.one = mixed_split(ms, R, S, H1, H2, true, kMixedBudget, kMixedMaxSplit);
+    // Small adapters: when an adapter's A is at most kSelfMaxA bytes and no
+    // tile has more than two column chunks, the one-launch form has no
+    // shrink items; each expand item computes its tile's v itself (at most
+    // twice per tile), which costs less than the hand-off's round trips.
+    int cmax = p.one.c[2];
+    if (ms.has_long) cmax = std::max(cmax, p.one.c[0]);
+    if (ms.has_short) cmax = std::max(cmax, p.one.c[1]);
+    if ((long long)H1 * ms.r * ms.e <= kSelfMaxA && cmax <= 2) {
+        for (int c = 0; c < 3; ++c) p.one.k[c] = 0;
+    }
     const long long q[3] = {p.one.k[0] + p.one.c[0], p.one.k[1] + p.one.c[1],
                             p.one.k[2] + p.one.c[2]};
     p.grid_one = mixed_bound(R, S, ms, q);

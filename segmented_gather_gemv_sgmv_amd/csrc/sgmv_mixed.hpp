@@ -265,6 +265,13 @@ struct VecTile {
         const st* Bj = b_ptr(B_stack, t.adapter, H2, j);
         uint4 bv[kKB];
         uint4 yv[RB];
+        if (ksplit == 0) {  // no shrink items (small adapters): v computed here
+            shrink_range(t, x, A_stack, H1, 0, H1, lds,
+                         [&](int i, int k, float v) { s_v[i * R + k] = v; });
+            expand_loads(bv, yv, Bj, y, t, j, active, H2);
+            expand_finish(bv, yv, Bj, y, t, j, active, H2, scale, s_v);
+            return;
+        }
         expand_loads(bv, yv, Bj, y, t, j, active, H2);
         if (tid == 0) *s_flag = wait_for_producers(cnt, ksplit, wait_ticks);
         __syncthreads();
@@ -444,6 +451,17 @@ struct MfmaTile {
         const st* B = B_stack + (long long)t.adapter * R * H2;
         st* yr = y + (long long)t.row0 * H2;
         ExpandRegs<R> er;
+        if (ksplit == 0) {  // no shrink items (small adapters): v computed here
+            for (int e = tid; e < kT * R; e += NT) sv[e] = 0.f;  // rows past the tile stay 0
+            __syncthreads();
+            for (int h_lo = 0; h_lo < H1; h_lo += kHMax)
+                shrink_chunk(t, x, A_stack, H1, h_lo, min(H1, h_lo + kHMax), lds,
+                             [&](int i, int k, float v) { sv[i * R + k] += v; });
+            expand_prefetch<DT, R>(er, B, yr, t.nrows, H2, c0);
+            expand_apply<DT, R>(er, s_a(lds), sv, s_vh(lds), s_max(lds), yr, t.nrows, H2, c0,
+                                scale, B);
+            return;
+        }
         expand_prefetch<DT, R>(er, B, yr, t.nrows, H2, c0);
         if (tid == 0) *s_flag = wait_for_producers(cnt, ksplit, wait_ticks);
         __syncthreads();

@@ -458,10 +458,42 @@ SELF_CONTAINED_CASES = {
     "mixed_small": lambda: wl.mixed_batch(3, long_rows=(40, 23, 2), short=60, H=2048, r=32,
                                           dtype="bf16", num_adapters=80),
     # float32: four-row vector tiles for the long segments, one-row tiles
-    "f32_vector_tiles": lambda: wl.make_workload("f32_mix", "f32", 1024, 768, 8, 12,
+    # (H1 = 2048: an adapter's A above the size whose tiles skip the hand-off)
+    "f32_vector_tiles": lambda: wl.make_workload("f32_mix", "f32", 2048, 768, 8, 12,
                                                  [1, 9, 1, 1, 4, 2, 1, 7], list(range(8)),
                                                  1.5, seed=4),
 }
+
+
+@pytest.mark.parametrize("dtype,H1,H2,r,lengths", [
+    ("f32", 256, 256, 8, [4, 4, 4, 4]),                       # the tiny config's shape
+    ("f16", 1024, 1000, 16, [1, 5, 0, 16, 2, 1, 9]),          # MFMA and one-row tiles
+    ("bf16", 512, 512, 32, [3, 1, 17, 1]),                    # 256-column expand items:
+    ("bf16", 256, 504, 64, [2, 1, 1, 30]),                    # two per tile, the second ragged
+    ("f16", 1000, 512, 8, [1, 3, 1, 6, 2]),                   # four-row vector tiles
+])
+def test_small_adapters_skip_the_handoff(dtype, H1, H2, r, lengths):
+    """When an adapter's A is small (<= 32 KB) and a tile has at most two
+    column chunks, the single launch has no shrink items: each expand item
+    computes its tile's v itself.  Parity with the oracle, and the counters
+    and the sticky flag are never touched, at the default patience and at
+    zero patience alike."""
+    import torch
+    import segmented_gather_gemv_sgmv_amd as sg
+    N = 5
+    ids = [(3 * k + 1) % N for k in range(len(lengths))]
+    w = wl.make_workload(f"small_{dtype}_{r}", dtype, H1, H2, r, N, lengths, ids, 1.25,
+                         seed=H1 + r)
+    y_ref, _ = oracle.lora_apply(w.y0, w.x, w.A, w.B, w.seg_indptr, w.adapter_ids, w.scale)
+    my, _ = magnitude(w)
+    y = gpu_lora_apply(w)
+    assert_close(y, y_ref, dtype, w.name, my)
+    try:
+        sg.set_fused_wait(0.0)
+        y0 = gpu_lora_apply(w)  # asserts the flag stays clear: nothing waited
+    finally:
+        sg.set_fused_wait(0.02)
+    assert np.array_equal(y, y0)
 
 
 @pytest.mark.parametrize("case", list(SELF_CONTAINED_CASES))
