@@ -603,6 +603,55 @@ int launch_status() {
     return SGMV_ERR_HIP;
 }
 
+// Whether a call's shrink fits the mixed two-launch form's shrink half, as a
+// pure function of the shapes (so that workspace sizes can be queried): ok,
+// and k, the largest number of H1 ranges of a class (k > 1: k partial
+// planes of [rows][r] floats, reduced into v by each tile's last workgroup
+// on the tile counters).
+struct MixedShrinkFit {
+    bool ok = false;
+    int k = 0;
+    MixedShape ms{};
+    MixedPlan xp{};
+};
+
+MixedShrinkFit mixed_shrink_fit(int M, int S, int H1, int r, int dtype) {
+    MixedShrinkFit f;
+    f.ms = mixed_shape(H1, 8, r, dtype);
+    if (!mixed_takes(f.ms, S)) return f;
+    f.xp = make_mixed_plan(f.ms, M, S, H1, 8);
+    f.k = std::max(std::max(f.xp.two_sp.k[0], f.xp.two_sp.k[1]), f.xp.two_sp.k[2]);
+    f.ok = f.xp.ok && (f.k == 1 || f.xp.tiles <= kCounterSlots);
+    return f;
+}
+
+bool mixed_shrink_aligned(const MixedShrinkFit& f, const void* x, const void* A_stack) {
+    return aligned16(A_stack) && (!f.ms.has_long || aligned16(x));
+}
+
+// v [rows][r] from the shrink half (partial planes at `part` and the tile
+// counters at `counters` when k > 1).
+void launch_mixed_shrink(const MixedShrinkFit& f, float* v, float* part, int* counters,
+                         const void* x, const void* A_stack, const int32_t* seg_indptr,
+                         const int32_t* adapter_ids, int S, int M, int num_adapters, int H1,
+                         int r, int dtype, hipStream_t st) {
+    const bool in_kernel = f.k > 1;
+    with_mixed(dtype, r, [&](auto dt, auto rank, auto lp, auto sp_, auto gp) {
+        using DT = decltype(dt);
+        using T = typename DT::storage;
+        constexpr int R = decltype(rank)::value;
+        using LP = decltype(lp);
+        using SP = decltype(sp_);
+        using GP = decltype(gp);
+        launch(&shrink_mixed_kernel<DT, R, LP, SP, GP>, dim3((unsigned)f.xp.grid_shrink),
+               dim3(kMixedThreads), st, (const T*)x, (const T*)A_stack, seg_indptr, adapter_ids,
+               S, M, num_adapters, H1, in_kernel ? part : v, f.xp.two_sp,
+               in_kernel ? v : (float*)nullptr, in_kernel ? counters : (int*)nullptr,
+               kCounterStride, (int4*)nullptr, 0);
+    });
+}
+
+
 // -- shrink dispatch ---------------------------------------------------------
 template <typename DT, int R>
 void launch_shrink_vec(float* out, long long out_stride, const void* x, const void* A,
@@ -743,23 +792,48 @@ bool grid_fits(const Plan& p, int H2) {
 using LinSkinny = LinearShape<1, 4, 4, 1, 4>;
 using LinSquare = LinearShape<2, 2, 4, 4, 2>;
 constexpr int kLinTargetWorkgroups = 256;  // split K until the grid has this many
+// 256 x 256 tiles (linear_wide_kernel) once they give at least half a tile
+// per compute unit, and the segments average at least this many rows (the
+// correction runs once per segment a tile overlaps).
+constexpr long long kLinWideMinTiles = 128;
+constexpr long long kLinWideMinRows = 32;
 
 struct LinearPlan {
-    int cfg;  // 0 skinny tiles, 1 square tiles, -1 the element-wise kernel
+    int cfg;  // 0 skinny tiles, 1 square tiles, 2 wide tiles, -1 the element-wise kernel
     int BM, BN;
     long long tiles_m, tiles_n, tiles;
     int ksplit, cps;  // K ranges per tile and chunks of 64 per range
-    Plan shrink;      // the preceding shrink launch (its ksplit = v's partials)
+    Plan shrink;      // the per-call shrink launch (its ksplit = v's partials)
+    int mix_planes;   // planes the mixed shrink needs (v and its partials), 0 if it does not fit
 };
 
 // Pure function of the shapes, so that the workspace size can be queried.
 LinearPlan make_linear_plan(int M, int S, int H1, int H2, int r, int dtype) {
     LinearPlan lp{};
     lp.shrink = make_plan(M, S, H1, r, dtype);
+    {
+        const MixedShrinkFit f = mixed_shrink_fit(M, S, H1, r, dtype);
+        lp.mix_planes = f.ok ? (f.k > 1 ? 1 + f.k : 1) : 0;
+    }
     lp.cfg = -1;
     lp.ksplit = 1;
     if (dtype == SGMV_F32 || H1 % 8 != 0 || H2 % 8 != 0) return lp;
     lp.cfg = M <= LinSkinny::kBM ? 0 : 1;
+    if (lp.cfg == 1) {
+        const long long tw =
+            (long long)((M + kWideBM - 1) / kWideBM) * ((H2 + kWideBN - 1) / kWideBN);
+        if (tw >= kLinWideMinTiles && (long long)S * kLinWideMinRows <= M) {
+            lp.cfg = 2;
+            lp.BM = kWideBM;
+            lp.BN = kWideBN;
+            lp.tiles_m = (M + kWideBM - 1) / kWideBM;
+            lp.tiles_n = (H2 + kWideBN - 1) / kWideBN;
+            lp.tiles = lp.tiles_m * lp.tiles_n;
+            lp.cps = (H1 + kLinBK - 1) / kLinBK;
+            lp.ksplit = 1;
+            return lp;
+        }
+    }
     lp.BM = lp.cfg == 0 ? LinSkinny::kBM : LinSquare::kBM;
     lp.BN = lp.cfg == 0 ? LinSkinny::kBN : LinSquare::kBN;
     lp.tiles_m = (M + lp.BM - 1) / lp.BM;
@@ -778,8 +852,10 @@ LinearPlan make_linear_plan(int M, int S, int H1, int H2, int r, int dtype) {
 }
 
 size_t linear_v_bytes(const LinearPlan& lp, int M, int r) {
-    // the shrink launch's chunk partials, or (folded) one per K range
-    const size_t planes = (size_t)std::max<long long>(lp.shrink.ksplit, lp.ksplit);
+    // the per-call shrink's chunk partials, or (folded) one per K range, or
+    // the mixed shrink's v and partials
+    const size_t planes = (size_t)std::max<long long>(
+        std::max<long long>(lp.shrink.ksplit, lp.ksplit), lp.mix_planes);
     return round256(planes * (size_t)M * (size_t)r * sizeof(float));
 }
 
@@ -960,37 +1036,16 @@ int sgmv_shrink(float* v, const void* x, const void* A_stack, const int32_t* seg
     // workspace); calls whose tiles could outnumber the counters keep the
     // per-call kernels.
     {
-        const MixedShape ms = mixed_shape(H1, 8, r, dtype);
-        const MixedPlan xp = mixed_takes(ms, num_segments)
-                                 ? make_mixed_plan(ms, num_rows, num_segments, H1, 8)
-                                 : MixedPlan{};
-        const int k = std::max(std::max(xp.two_sp.k[0], xp.two_sp.k[1]), xp.two_sp.k[2]);
-        if (xp.ok && (k == 1 || xp.tiles <= kCounterSlots) && aligned16(A_stack) &&
-            (!ms.has_long || aligned16(x))) {
-            {
-                const MixedSplit& sp = xp.two_sp;
-                const size_t need_m = k > 1 ? kCounterBytes + (size_t)k * (size_t)num_rows *
-                                                                  (size_t)r * sizeof(float)
-                                            : 0;
-                if (need_m > 0 && (!workspace || workspace_bytes < need_m))
-                    return SGMV_ERR_WORKSPACE;
-                float* part = k > 1 ? (float*)((char*)workspace + kCounterBytes) : v;
-                const bool in_kernel = k > 1;
-                with_mixed(dtype, r, [&](auto dt, auto rank, auto lp, auto sp_, auto gp) {
-                    using DT = decltype(dt);
-                    using T = typename DT::storage;
-                    constexpr int R = decltype(rank)::value;
-                    using LP = decltype(lp);
-                    using SP = decltype(sp_);
-                    using GP = decltype(gp);
-                    launch(&shrink_mixed_kernel<DT, R, LP, SP, GP>, dim3((unsigned)xp.grid_shrink),
-                           dim3(kMixedThreads), st, (const T*)x, (const T*)A_stack, seg_indptr,
-                           adapter_ids, num_segments, num_rows, num_adapters, H1, part, sp,
-                           in_kernel ? v : (float*)nullptr, in_kernel ? (int*)workspace : nullptr,
-                           kCounterStride, (int4*)nullptr, 0);
-                });
-                return launch_status();
-            }
+        const MixedShrinkFit f = mixed_shrink_fit(num_rows, num_segments, H1, r, dtype);
+        if (f.ok && mixed_shrink_aligned(f, x, A_stack)) {
+            const size_t need_m = f.k > 1 ? kCounterBytes + (size_t)f.k * (size_t)num_rows *
+                                                                (size_t)r * sizeof(float)
+                                          : 0;
+            if (need_m > 0 && (!workspace || workspace_bytes < need_m)) return SGMV_ERR_WORKSPACE;
+            launch_mixed_shrink(f, v, f.k > 1 ? (float*)((char*)workspace + kCounterBytes) : v,
+                                (int*)workspace, x, A_stack, seg_indptr, adapter_ids,
+                                num_segments, num_rows, num_adapters, H1, r, dtype, st);
+            return launch_status();
         }
     }
     float* out = p.ksplit > 1 ? (float*)((char*)workspace + kCounterBytes) : v;
@@ -1501,11 +1556,22 @@ int lora_linear(void* y, const void* x, const void* W, const void* bias, const v
     // Decode tiles fold the shrink into their own launch (linear_lora_kernel).
     const bool fold =
         tiled && aligned16(A_stack) && linear_folds(lp, num_rows, num_segments, r, dtype);
-    const int vsplit = fold ? lp.ksplit : lp.shrink.ksplit;
+    int vsplit = fold ? lp.ksplit : lp.shrink.ksplit;
     const double wait_s = fused_wait_seconds();
     const long long wait =
         wait_s < 1e-300 ? -1 : (long long)(wait_s * (double)wall_ticks_per_second());
-    if (num_segments > 0 && !fold) {
+    // The shrink: the mixed two-launch form's shrink half when it fits (v
+    // finished in plane 0, its partials after it; the tile counters it uses
+    // return to zero), else the per-call kernels' chunk partials.
+    const MixedShrinkFit mf = num_segments > 0 && !fold && lp.mix_planes > 0
+                                  ? mixed_shrink_fit(num_rows, num_segments, H1, r, dtype)
+                                  : MixedShrinkFit{};
+    if (mf.ok && mixed_shrink_aligned(mf, x, A_stack)) {
+        launch_mixed_shrink(mf, vpart, vpart + vstride, counters, x, A_stack, seg_indptr,
+                            adapter_ids, num_segments, num_rows, num_adapters, H1, r, dtype, st);
+        if ((rc = launch_status()) != SGMV_OK) return rc;
+        vsplit = 1;
+    } else if (num_segments > 0 && !fold) {
         with_dtype(dtype, [&](auto dt) {
             using DT = decltype(dt);
             dispatch_shrink<DT>(vpart, vstride, x, A_stack, seg_indptr, adapter_ids, num_segments,
@@ -1525,7 +1591,13 @@ int lora_linear(void* y, const void* x, const void* W, const void* bias, const v
                 return;
             }
             if (tiled) {
-                if (lp.cfg == 0)
+                if (lp.cfg == 2)
+                    launch(&linear_wide_kernel<DT>, dim3((unsigned)lp.tiles),
+                           dim3(kWideThreads), st, (T*)y, (const T*)x, (const T*)W,
+                           (const T*)bias, (const T*)B_stack, (const float*)vpart, vstride,
+                           vsplit, seg_indptr, adapter_ids, num_segments, num_rows, num_adapters,
+                           H1, H2, r, scale, (int)lp.tiles_n, (int)lp.tiles);
+                else if (lp.cfg == 0)
                     launch_linear_tiled<DT, LinSkinny>(y, x, W, bias, B_stack, vpart, vstride,
                                                        vsplit, seg_indptr, adapter_ids,
                                                        num_segments, num_rows, num_adapters, H1,

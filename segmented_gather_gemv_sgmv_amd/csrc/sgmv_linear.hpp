@@ -44,6 +44,8 @@
 #include "sgmv_fused.hpp"
 #include "sgmv_mfma.hpp"
 
+#include <type_traits>
+
 namespace sgmv {
 
 constexpr int kLinThreads = 256;
@@ -712,6 +714,373 @@ __global__ __launch_bounds__(kLinThreads) void linear_lora_kernel(
         s_t, s_aid, s_v, s_seg, s_ids, &s_last, seg_lds, y, bias, B_stack, vpart, vstride, vsplit,
         seg_indptr, adapter_ids, S, M, num_adapters, H2, r, scale, part, counters, counter_stride,
         ksplit, q, t, m0, n0, bpre);
+}
+
+// ---- many rows: 256 x 256 tiles ----------------------------------------------
+// For batches of many rows (prefill) the base product dominates and the tile
+// size sets how often x and W are re-read from L2: with 256 x 256 tiles a
+// 4096 x 4096 output is 256 tiles, one per compute unit, each reading its 256
+// rows of x and of W once.  A workgroup is 512 threads (eight waves, two per
+// SIMD, each owning 128 rows x 64 columns of the tile, 8 x 4 MFMA blocks).
+//
+// K moves in chunks of 64 through two LDS buffers (x rows in one array, W
+// rows in another, 32 KB each), loaded through registers one chunk ahead.
+// In LDS each 128-byte row keeps its 16-byte piece p at p ^ (row & 7), which
+// spreads the rows an MFMA operand read touches over the banks.
+//
+// The product is computed transposed, Y^T = W X^T (W as the MFMA's A
+// operand), so that each lane's accumulator holds four consecutive columns
+// of one row: the epilogue adds the bias and stores 8-byte pieces of y
+// straight from the registers.
+//
+// The correction s (x A_a) B_a runs on the same accumulators, also on the
+// matrix cores, one segment of the tile at a time: for ranks in passes of
+// 16, D += B'^T V'^T with the rows outside the segment masked to zero in V'.
+// The 16-bit MFMA operands carry float32 precision through term splits in
+// bf16 (whose exponent range is float32's, so no scaling is needed):
+// s v = vh + vm + vl (three bf16 terms, 24 significant bits) and, for fp16
+// weights, B = Bh + Bl exactly (11 significant bits in two bf16 terms).  The
+// K dimension pairs them as [vh Bh | vm Bh | vl Bh | vh Bl | vm Bl | 0]
+// (fp16; the dropped vl Bl is below float32 rounding of the product) or
+// [vh B | vm B | vl B | 0] (bf16), in MFMA steps of 32.
+constexpr int kWideThreads = 512;
+constexpr int kWideBM = 256, kWideBN = 256;        // tile
+constexpr int kWideTM = 8, kWideTN = 4;            // 16 x 16 blocks per wave
+constexpr int kWideWN = kWideBN / (16 * kWideTN);  // waves along the columns
+constexpr int kWideBK = 64;                        // K per chunk
+constexpr int kWideHalf = kWideBM * kWideBK;       // 16-bit elements of one operand's chunk
+constexpr int kWideRG = 16;                        // ranks per correction pass
+constexpr int kWideLdB = kWideBN + 16;  // padded row of B' (transposing reads)
+constexpr int kWideSegLds = kWideThreads - 1;  // segment-table entries staged in LDS
+static_assert(kWideBM == kWideBN, "square tile");
+static_assert((kWideBM / (16 * kWideTM)) * kWideWN * kWave == kWideThreads, "eight waves");
+
+template <typename DT>
+struct WideTerms;
+template <>
+struct WideTerms<F16> {
+    static constexpr int kK = 96;  // five products of 16 ranks, padded to 3 MFMA steps
+};
+template <>
+struct WideTerms<BF16> {
+    static constexpr int kK = 64;  // three products of 16 ranks, padded to 2 steps
+};
+
+// LDS: buffer 0 is (s_wide0: x rows, s_wide1: W rows), buffer 1 is
+// (s_wide2, s_wide3); the correction reuses all four.
+__shared__ __attribute__((aligned(16))) uint16_t s_wide0[kWideHalf];
+__shared__ __attribute__((aligned(16))) uint16_t s_wide1[kWideHalf];
+__shared__ __attribute__((aligned(16))) uint16_t s_wide2[kWideHalf];
+__shared__ __attribute__((aligned(16))) uint16_t s_wide3[kWideHalf];
+
+// bf16 terms of a float: hi, and the rounded remainder (0 for inf / NaN,
+// whose remainder is not a number).
+__device__ __forceinline__ uint32_t bf16_rest(float f, uint32_t hi) {
+    return (hi & 0x7F80u) == 0x7F80u ? 0u : BF16::f2b(f - BF16::b2f(hi));
+}
+
+// Grid: exactly `tiles` workgroups.  Workgroup b runs on XCD b % 8; when the
+// tile count is a multiple of 8, each XCD takes a contiguous range of tiles
+// (whole rows of tiles at the usual shapes), so its L2 serves the x rows
+// those tiles share.  H1 and H2 are multiples of 8; x, W, y and bias are
+// 16-byte aligned.
+template <typename DT>
+__global__ __launch_bounds__(kWideThreads) void linear_wide_kernel(
+    typename DT::storage* __restrict__ y, const typename DT::storage* __restrict__ x,
+    const typename DT::storage* __restrict__ W, const typename DT::storage* __restrict__ bias,
+    const typename DT::storage* __restrict__ B_stack, const float* __restrict__ vpart,
+    long long vstride, int vsplit, const int* __restrict__ seg_indptr,
+    const int* __restrict__ adapter_ids, int S, int M, int num_adapters, int H1, int H2, int r,
+    float scale, int tiles_n, int tiles) {
+    using T = typename DT::storage;
+    using Ops = MfmaOps<DT>;
+    using BOps = MfmaOps<BF16>;
+    constexpr int KQ = WideTerms<DT>::kK;
+    constexpr int VQ = KQ + 8;  // padded row of V' (bank spread of the operand reads)
+    constexpr bool kSplitB = std::is_same<DT, F16>::value;
+    // Epilogue: V' rows [0, 128) in stage 0 and [128, 256) in stage 1, B'
+    // rows [0, KQ / 2) in stage 2 and the rest in stage 3.
+    static_assert(kWideBM / 2 * VQ <= kWideHalf && KQ / 2 * kWideLdB <= kWideHalf,
+                  "V' and B' fit the buffers");
+    static_assert((KQ / 2) % 8 == 0, "an operand's 8 rows of B' lie in one stage");
+    __shared__ __attribute__((aligned(16))) float s_v[kWideBM * kWideRG];
+    __shared__ int s_seg[kWideSegLds + 1];
+    __shared__ int s_ids[kWideSegLds];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wid = tid / kWave;
+    const int lr = lane & 15, lg = lane >> 4;
+    int t = (int)blockIdx.x;
+    if ((tiles & 7) == 0) t = (t & 7) * (tiles >> 3) + (t >> 3);
+    if (t >= tiles) return;  // whole workgroup (the grid is exact)
+    const int m0 = (t / tiles_n) * kWideBM;
+    const int n0 = (t % tiles_n) * kWideBN;
+    const int nchunks = (H1 + kWideBK - 1) / kWideBK;
+    const int wr0 = (wid / kWideWN) * (16 * kWideTM);  // first tile row of this wave
+    const int wc0 = (wid % kWideWN) * (16 * kWideTN);  // first tile column of this wave
+
+    // The segment table when it fits LDS.
+    const bool seg_lds = S <= kWideSegLds;  // no table is read when S == 0
+    if (seg_lds && S > 0) {
+        if (tid <= S) s_seg[tid] = seg_indptr[tid];
+        if (tid < S) s_ids[tid] = adapter_ids[tid];
+    }
+    __syncthreads();
+    auto seg_at = [&](int s) { return seg_lds ? s_seg[s] : seg_indptr[s]; };
+    auto id_at = [&](int s) { return seg_lds ? s_ids[s] : adapter_ids[s]; };
+    const int row_end = min(m0 + kWideBM, M);
+    // The next segment from s on that covers rows of this tile and has a
+    // valid adapter (S if none).  Uniform over the workgroup.
+    auto next_segment = [&](int s) {
+        for (; s < S; ++s) {
+            const int lo = seg_at(s);
+            if (lo >= row_end) return S;
+            const int hi = min(seg_at(s + 1), row_end);
+            const int a = id_at(s);
+            if (hi > max(lo, m0) && a >= 0 && a < num_adapters) return s;
+        }
+        return S;
+    };
+    // First segment ending after m0 (segment ends are non-decreasing).
+    int first = 0;
+    {
+        int lo = 0, hi = S;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (seg_at(mid + 1) <= m0) lo = mid + 1;
+            else hi = mid;
+        }
+        first = lo;
+    }
+    // The first pass of v (before the main loop, whose loads it overlaps).
+    auto fill_v = [&](int g0) {
+        for (int e = tid; e < kWideBM * kWideRG; e += kWideThreads) {
+            const int il = e / kWideRG, k = e % kWideRG;
+            float v = 0.f;
+            if (m0 + il < M && g0 + k < r)
+                v = sum_partials(vpart + (long long)(m0 + il) * r + g0 + k, vstride, vsplit);
+            s_v[e] = v;
+        }
+    };
+    if (next_segment(first) < S) fill_v(0);  // uniform; tiles without adapted rows skip it
+
+    // ---- base product ------------------------------------------------------
+    // A chunk of one operand is 256 rows x 8 pieces of 16 bytes: 4 pieces
+    // per thread.
+    constexpr int kP = kWideBM * (kWideBK / 8) / kWideThreads;
+    static_assert(kP * kWideThreads == kWideBM * (kWideBK / 8), "whole pieces per thread");
+    uint4 ring[2 * kP];  // one chunk: this thread's pieces of x rows, then of W rows
+    auto load_chunk = [&](int c) {
+        const int k0 = c * kWideBK;
+#pragma unroll
+        for (int u = 0; u < kP; ++u) {
+            const int id = tid + u * kWideThreads;
+            const int row = id >> 3, gk = k0 + (id & 7) * 8;
+            ring[u] = (m0 + row < M && gk < H1) ? load16(x + (long long)(m0 + row) * H1 + gk)
+                                                : make_uint4(0, 0, 0, 0);
+            ring[kP + u] = (n0 + row < H2 && gk < H1)
+                               ? load16(W + (long long)(n0 + row) * H1 + gk)
+                               : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto store_chunk = [&](uint16_t* sx, uint16_t* sw) {
+#pragma unroll
+        for (int u = 0; u < kP; ++u) {
+            const int id = tid + u * kWideThreads;
+            const int row = id >> 3, p = id & 7;  // row < kWideBM: off < kWideHalf
+            const int off = row * kWideBK + ((p ^ (row & 7)) << 3);
+            *reinterpret_cast<uint4*>(sx + off) = ring[u];
+            *reinterpret_cast<uint4*>(sw + off) = ring[kP + u];
+        }
+    };
+
+    mf32x4 acc[kWideTM][kWideTN];
+#pragma unroll
+    for (int i = 0; i < kWideTM; ++i)
+#pragma unroll
+        for (int j = 0; j < kWideTN; ++j) acc[i][j] = mf32x4{0.f, 0.f, 0.f, 0.f};
+
+    // One chunk: two K steps of 32, each the wave's 4 W blocks against its 8
+    // x blocks.
+    auto compute = [&](const uint16_t* sx, const uint16_t* sw) {
+        auto rd = [&](const uint16_t* base, int row, int ks) {
+            const int p = 4 * ks + lg;  // 16-byte piece of the 32-k step
+            return *reinterpret_cast<const uint4*>(base + row * kWideBK + ((p ^ (row & 7)) << 3));
+        };
+        uint4 b0[kWideTN], b1[kWideTN];
+#pragma unroll
+        for (int j = 0; j < kWideTN; ++j) b0[j] = rd(sw, wc0 + 16 * j + lr, 0);
+        uint4 a = rd(sx, wr0 + lr, 0);
+#pragma unroll
+        for (int i = 0; i < kWideTM; ++i) {
+            const uint4 an = rd(sx, wr0 + 16 * ((i + 1) % kWideTM) + lr, i + 1 < kWideTM ? 0 : 1);
+            if (i == kWideTM / 2) {
+#pragma unroll
+                for (int j = 0; j < kWideTN; ++j) b1[j] = rd(sw, wc0 + 16 * j + lr, 1);
+            }
+#pragma unroll
+            for (int j = 0; j < kWideTN; ++j) acc[i][j] = Ops::mma(b0[j], a, acc[i][j]);
+            a = an;
+        }
+#pragma unroll
+        for (int i = 0; i < kWideTM; ++i) {
+            uint4 an = a;
+            if (i + 1 < kWideTM) an = rd(sx, wr0 + 16 * (i + 1) + lr, 1);
+#pragma unroll
+            for (int j = 0; j < kWideTN; ++j) acc[i][j] = Ops::mma(b1[j], a, acc[i][j]);
+            a = an;
+        }
+    };
+    // Chunk c: its registers into buffer c % 2 (every wave is past the
+    // barrier of chunk c - 1, so done with chunk c - 2 there), the next
+    // chunk's loads issued, then the barrier and the MFMAs.
+    auto chunk = [&](int c, uint16_t* sx, uint16_t* sw) {
+        store_chunk(sx, sw);
+        if (c + 1 < nchunks) load_chunk(c + 1);
+        lds_barrier();
+        compute(sx, sw);
+    };
+    load_chunk(0);
+    for (int c = 0; c < nchunks; c += 2) {
+        chunk(c, s_wide0, s_wide1);
+        if (c + 1 < nchunks) chunk(c + 1, s_wide2, s_wide3);
+    }
+
+    // ---- correction ---------------------------------------------------------
+    auto vq_row = [&](int il) {  // row il of V'
+        return il < kWideBM / 2 ? s_wide0 + il * VQ : s_wide1 + (il - kWideBM / 2) * VQ;
+    };
+    auto bq_row = [&](int k) {  // row k of B'
+        return k < KQ / 2 ? s_wide2 + k * kWideLdB : s_wide3 + (k - KQ / 2) * kWideLdB;
+    };
+    // This thread's piece of a B' pass: rank tid / 32, columns (tid % 32) * 8.
+    const int bk = tid >> 5, bc = n0 + (tid & 31) * 8;
+    auto load_b = [&](int s, int g0) {
+        const int a = id_at(s);
+        return (g0 + bk < r && bc < H2)
+                   ? load16(B_stack + ((long long)a * r + g0 + bk) * H2 + bc)
+                   : make_uint4(0, 0, 0, 0);
+    };
+    int seg_cur = next_segment(first);
+    uint4 braw = seg_cur < S ? load_b(seg_cur, 0) : make_uint4(0, 0, 0, 0);
+    for (int g0 = 0; g0 < r && seg_cur < S; g0 += kWideRG) {
+        // The stages (and, from the second pass, s_v) are free: every wave is
+        // past its last step and, by the barrier's fence (vmcnt(0)), its
+        // loads into the stages have landed.
+        __syncthreads();
+        if (g0 > 0) {
+            fill_v(g0);
+            __syncthreads();
+        }
+        // V' rows: the terms of s v in the slot order of B'.
+        for (int e = tid; e < kWideBM * kWideRG; e += kWideThreads) {
+            const int il = e / kWideRG, k = e % kWideRG;
+            const float v = scale * s_v[e];
+            const uint32_t vh = BF16::f2b(v);
+            const uint32_t vm = bf16_rest(v, vh);
+            const float r1 = (vh & 0x7F80u) == 0x7F80u ? 0.f : v - BF16::b2f(vh);
+            const uint32_t vl = bf16_rest(r1, vm);
+            uint16_t* q = vq_row(il);
+            q[k] = (uint16_t)vh;
+            q[kWideRG + k] = (uint16_t)vm;
+            q[2 * kWideRG + k] = (uint16_t)vl;
+            if constexpr (kSplitB) {
+                q[3 * kWideRG + k] = (uint16_t)vh;
+                q[4 * kWideRG + k] = (uint16_t)vm;
+                q[5 * kWideRG + k] = 0;
+            } else {
+                q[3 * kWideRG + k] = 0;
+            }
+        }
+        if (g0 > 0) braw = load_b(seg_cur, g0);
+        while (seg_cur < S) {
+            __syncthreads();  // V' written; the previous segment's reads of B' done
+            {
+                float f[8];
+                DT::unpack(braw, f);
+                uint4 hi, lo;
+                if constexpr (kSplitB) {
+                    uint32_t h[8], l[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        h[e] = BF16::f2b(f[e]);
+                        l[e] = bf16_rest(f[e], h[e]);
+                    }
+                    hi = make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16,
+                                    h[6] | h[7] << 16);
+                    lo = make_uint4(l[0] | l[1] << 16, l[2] | l[3] << 16, l[4] | l[5] << 16,
+                                    l[6] | l[7] << 16);
+                } else {
+                    hi = braw;
+                    lo = make_uint4(0, 0, 0, 0);
+                }
+                const int c8 = (tid & 31) * 8;
+                store16(bq_row(bk) + c8, hi);
+                store16(bq_row(kWideRG + bk) + c8, hi);
+                store16(bq_row(2 * kWideRG + bk) + c8, hi);
+                if constexpr (kSplitB) {
+                    store16(bq_row(3 * kWideRG + bk) + c8, lo);
+                    store16(bq_row(4 * kWideRG + bk) + c8, lo);
+                    store16(bq_row(5 * kWideRG + bk) + c8, make_uint4(0, 0, 0, 0));
+                } else {
+                    store16(bq_row(3 * kWideRG + bk) + c8, make_uint4(0, 0, 0, 0));
+                }
+            }
+            __syncthreads();
+            const int lo_row = max(seg_at(seg_cur), m0);
+            const int hi_row = min(seg_at(seg_cur + 1), row_end);
+            const int seg_next = next_segment(seg_cur + 1);
+            if (seg_next < S) braw = load_b(seg_next, g0);  // in flight during the MFMAs
+#pragma unroll
+            for (int ks = 0; ks < KQ / 32; ++ks) {
+                // this lane group's 8 rows of B' (one stage holds all of them)
+                const int k0 = ks * 32 + lg * 8;
+                const uint16_t* bbase = k0 < KQ / 2 ? s_wide2 : s_wide3;
+                const int kl = k0 < KQ / 2 ? k0 : k0 - KQ / 2;
+                uint4 bb[kWideTN];
+#pragma unroll
+                for (int j = 0; j < kWideTN; ++j)
+                    bb[j] = lds_operand_tr(bbase + wc0 + 16 * j, kl, kWideLdB, lr);
+#pragma unroll
+                for (int i = 0; i < kWideTM; ++i) {
+                    const int rb = m0 + wr0 + 16 * i;
+                    if (rb + 16 <= lo_row || rb >= hi_row) continue;  // uniform over the wave
+                    const int row = rb + lr;
+                    const uint4 vv = (row >= lo_row && row < hi_row)
+                                         ? *reinterpret_cast<const uint4*>(
+                                               vq_row(wr0 + 16 * i + lr) + ks * 32 + lg * 8)
+                                         : make_uint4(0, 0, 0, 0);
+#pragma unroll
+                    for (int j = 0; j < kWideTN; ++j) acc[i][j] = BOps::mma(bb[j], vv, acc[i][j]);
+                }
+            }
+            seg_cur = seg_next;
+        }
+        seg_cur = next_segment(first);
+        if (g0 + kWideRG >= r) break;
+    }
+
+    // ---- bias, one rounding, store ------------------------------------------
+#pragma unroll
+    for (int j = 0; j < kWideTN; ++j) {
+        const int col = n0 + wc0 + 16 * j + 4 * lg;
+        if (col >= H2) continue;
+        float bv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (bias) {
+            const uint2 braw2 = load8(bias + col);
+            DT::unpack2(braw2.x, bv);
+            DT::unpack2(braw2.y, bv + 2);
+        }
+#pragma unroll
+        for (int i = 0; i < kWideTM; ++i) {
+            const int row = m0 + wr0 + 16 * i + lr;
+            if (row >= M) continue;
+            const uint2 o = make_uint2(DT::pack2(acc[i][j][0] + bv[0], acc[i][j][1] + bv[1]),
+                                       DT::pack2(acc[i][j][2] + bv[2], acc[i][j][3] + bv[3]));
+            store8(y + (long long)row * H2 + col, o);
+        }
+    }
 }
 
 // Any shape and dtype: one thread per output element, the base product as

@@ -3,9 +3,9 @@ fused in) against the fp64 CPU oracle.
 
 y = x W^T + bias + scale * (x A_a) B_a per row of each segment, base product
 only elsewhere; tolerances as for the add-on (tests/gpu_helpers.py).  The
-cases reach both tile shapes of the matrix-core kernel (64 x 64 tiles whose
-K range is split over workgroups, and 128 x 128 tiles), ragged row, column
-and K tails, and the element-wise kernel (float32, misaligned pointers,
+cases reach the three tile shapes of the matrix-core kernels (64 x 64 tiles
+whose K range is split over workgroups, 128 x 128 tiles, and 256 x 256 tiles
+for many rows), ragged row, column and K tails, and the element-wise kernel (float32, misaligned pointers,
 sizes not a multiple of 8).
 """
 from __future__ import annotations
@@ -236,6 +236,72 @@ def test_prefill_tiling_every_row():
     print("lora_linear prefill tiling 4096 x 1024 -> 512", flush=True)
     assert_close(_gpu_linear(w, W, b), _oracle(w, W, b), w.dtype, "prefill tiling",
                  _oracle(w, W, b, absolute=True))
+
+
+# 256 x 256 tiles (linear_wide_kernel): at least 128 tiles and segments of
+# 32 or more rows on average.  (seed, dtype, H1, H2, r, N, R, S, uncovered
+# tail, bias)
+WIDE_CASES = [
+    (41, "f16", 264, 4088, 16, 8, 2000, 12, 7, True),   # ragged rows, columns, K chunk
+    (42, "bf16", 256, 4096, 16, 6, 2048, 16, 0, True),  # bf16
+    (43, "f16", 128, 2048, 40, 5, 4096, 24, 0, False),  # rank passes 16 + 16 + 8, no bias
+    (44, "bf16", 128, 4096, 128, 3, 2100, 4, 30, True),  # r = 128, uncovered tail rows
+]
+
+
+@pytest.mark.parametrize("case", WIDE_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_wide_tiles_every_element(case):
+    """Every element of the 256 x 256 tile path against the oracle, and a
+    second call bit for bit equal to the first."""
+    seed, dtype, H1, H2, r, N, R, S, tail, bias = case
+    w = wl.small_random(seed, dtype, H1, H2, r, N, R, S, uncovered_tail=tail)
+    W, b = wl.base_layer(seed, dtype, H1, H2, bias=bias)
+    d = to_device(w)
+    print(f"lora_linear wide tiles {case}", flush=True)
+    got = _gpu_linear(w, W, b, d)
+    assert_close(got, _oracle(w, W, b), dtype, str(case), _oracle(w, W, b, absolute=True))
+    assert np.array_equal(_gpu_linear(w, W, b, d), got)
+
+
+def test_wide_tiles_integer_inputs_bit_for_bit():
+    """Exact integers through the 256 x 256 tiles: the correction's bf16
+    terms of v and of the fp16 weights add up exactly, so y must equal the
+    oracle's value bit for bit."""
+    w = wl.integer_exact(11, "f16", 64, 4096, 16, 5, 2048, 6, density=0.2, scale=2.0)
+    W, b = wl.base_layer(11, "f16", 64, 4096, integer=True, density=0.2)
+    ref = _oracle(w, W, b)
+    assert np.abs(ref).max() <= 2048, "inputs leave the exactly representable range"
+    assert np.array_equal(_gpu_linear(w, W, b), ref)
+
+
+def test_wide_tiles_invalid_adapters_and_null_tables():
+    """Segments naming no adapter get the base product; with no segments and
+    NULL tables the wide tiles return the base layer."""
+    import torch
+    import segmented_gather_gemv_sgmv_amd as sg
+    w = wl.small_random(45, "f16", 128, 4096, 16, 4, 2048, 6, allow_empty=False)
+    W, b = wl.base_layer(45, "f16", 128, 4096)
+    ids = w.adapter_ids.copy()
+    ids[1], ids[4] = -1, 4
+    got = _gpu_linear(w, W, b, ids=torch.from_numpy(ids).to("cuda:0"))
+    ref = _oracle(w, W, b)
+    ref_base = _oracle(w, W, b, np.zeros(1, np.int32), np.zeros(0, np.int32))
+    for s in range(6):
+        lo, hi = int(w.seg_indptr[s]), int(w.seg_indptr[s + 1])
+        want = ref_base[lo:hi] if s in (1, 4) else ref[lo:hi]
+        assert_close(got[lo:hi], want, "f16", f"segment {s}")
+    rows, H1, H2 = w.num_rows, w.H1, w.H2
+    x, Wd, bd = _dev(w.x, "f16"), _dev(W, "f16"), _dev(b, "f16")
+    y = torch.full((rows, H2), 7.0, dtype=torch.float16, device="cuda:0")
+    lib = sg.lib()
+    need = int(lib.lora_linear_workspace_bytes(rows, 0, H1, H2, 16, sg.SGMV_F16))
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda:0")
+    rc = lib.lora_linear(y.data_ptr(), x.data_ptr(), Wd.data_ptr(), bd.data_ptr(), None, None,
+                         None, None, 0, rows, 0, H1, H2, 16, 2.0, sg.SGMV_F16, ws.data_ptr(),
+                         ws.numel(), torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, sg.STATUS.get(rc, rc)
+    torch.cuda.synchronize()
+    assert_close(y.double().cpu().numpy(), ref_base, "f16", "S=0, NULL tables")
 
 
 def test_repeated_calls_are_bitwise_identical():
