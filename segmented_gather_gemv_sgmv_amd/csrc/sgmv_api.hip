@@ -797,6 +797,7 @@ constexpr int kLinTargetWorkgroups = 256;  // split K until the grid has this ma
 // correction runs once per segment a tile overlaps).
 constexpr long long kLinWideMinTiles = 128;
 constexpr long long kLinWideMinRows = 32;
+using LinWide = WideShape<4, 1>;
 
 struct LinearPlan {
     int cfg;  // 0 skinny tiles, 1 square tiles, 2 wide tiles, -1 the element-wise kernel
@@ -1592,8 +1593,8 @@ int lora_linear(void* y, const void* x, const void* W, const void* bias, const v
             }
             if (tiled) {
                 if (lp.cfg == 2)
-                    launch(&linear_wide_kernel<DT>, dim3((unsigned)lp.tiles),
-                           dim3(kWideThreads), st, (T*)y, (const T*)x, (const T*)W,
+                    launch(&linear_wide_kernel<DT, LinWide>, dim3((unsigned)lp.tiles),
+                           dim3(LinWide::kNT), st, (T*)y, (const T*)x, (const T*)W,
                            (const T*)bias, (const T*)B_stack, (const float*)vpart, vstride,
                            vsplit, seg_indptr, adapter_ids, num_segments, num_rows, num_adapters,
                            H1, H2, r, scale, (int)lp.tiles_n, (int)lp.tiles);

@@ -720,11 +720,12 @@ __global__ __launch_bounds__(kLinThreads) void linear_lora_kernel(
 // For batches of many rows (prefill) the base product dominates and the tile
 // size sets how often x and W are re-read from L2: with 256 x 256 tiles a
 // 4096 x 4096 output is 256 tiles, one per compute unit, each reading its 256
-// rows of x and of W once.  A workgroup is 512 threads (eight waves, two per
-// SIMD, each owning 128 rows x 64 columns of the tile, 8 x 4 MFMA blocks).
+// rows of x and of W once.  A workgroup is one of the WideShape forms below:
+// eight waves of 128 rows x 64 columns, or four of 128 x 128.
 //
 // K moves in chunks of 64 through two LDS buffers (x rows in one array, W
-// rows in another, 32 KB each), loaded through registers one chunk ahead.
+// rows in another, 32 KB each), loaded through registers one or two chunks
+// ahead.
 // In LDS each 128-byte row keeps its 16-byte piece p at p ^ (row & 7), which
 // spreads the rows an MFMA operand read touches over the banks.
 //
@@ -743,17 +744,29 @@ __global__ __launch_bounds__(kLinThreads) void linear_lora_kernel(
 // K dimension pairs them as [vh Bh | vm Bh | vl Bh | vh Bl | vm Bl | 0]
 // (fp16; the dropped vl Bl is below float32 rounding of the product) or
 // [vh B | vm B | vl B | 0] (bf16), in MFMA steps of 32.
-constexpr int kWideThreads = 512;
 constexpr int kWideBM = 256, kWideBN = 256;        // tile
-constexpr int kWideTM = 8, kWideTN = 4;            // 16 x 16 blocks per wave
-constexpr int kWideWN = kWideBN / (16 * kWideTN);  // waves along the columns
+constexpr int kWideTM = 8;                         // 16-row blocks per wave: 128 rows
 constexpr int kWideBK = 64;                        // K per chunk
 constexpr int kWideHalf = kWideBM * kWideBK;       // 16-bit elements of one operand's chunk
 constexpr int kWideRG = 16;                        // ranks per correction pass
 constexpr int kWideLdB = kWideBN + 16;  // padded row of B' (transposing reads)
-constexpr int kWideSegLds = kWideThreads - 1;  // segment-table entries staged in LDS
 static_assert(kWideBM == kWideBN, "square tile");
-static_assert((kWideBM / (16 * kWideTM)) * kWideWN * kWave == kWideThreads, "eight waves");
+
+// Workgroup shapes of the 256 x 256 tile: TN 16-column blocks per wave (two
+// waves along the rows, 256 / (16 TN) along the columns) and PD chunks of
+// loads in flight.  <4, 1>: eight waves of 128 x 64, two per SIMD (the one
+// in use).  <8, 1> and <8, 2>: four waves of 128 x 128, one per SIMD with
+// the accumulators in AGPRs; they read a third fewer LDS bytes per MFMA, but
+// with one wave per SIMD nothing hides a wave's own waits, and at 4096 x
+// 4096 x 4096 they took 205 and 218 us against 187 us for <4, 1>.
+template <int TN_, int PD_>
+struct WideShape {
+    static constexpr int TN = TN_, PD = PD_;
+    static constexpr int WN = kWideBN / (16 * TN);  // waves along the columns
+    static constexpr int kNT = 2 * WN * kWave;      // threads
+    static constexpr int kSegLds = kNT - 1;         // segment-table entries staged in LDS
+    static_assert(2 * 16 * kWideTM == kWideBM, "two waves along the rows");
+};
 
 template <typename DT>
 struct WideTerms;
@@ -784,8 +797,8 @@ __device__ __forceinline__ uint32_t bf16_rest(float f, uint32_t hi) {
 // (whole rows of tiles at the usual shapes), so its L2 serves the x rows
 // those tiles share.  H1 and H2 are multiples of 8; x, W, y and bias are
 // 16-byte aligned.
-template <typename DT>
-__global__ __launch_bounds__(kWideThreads) void linear_wide_kernel(
+template <typename DT, typename WS>
+__global__ __launch_bounds__(WS::kNT) void linear_wide_kernel(
     typename DT::storage* __restrict__ y, const typename DT::storage* __restrict__ x,
     const typename DT::storage* __restrict__ W, const typename DT::storage* __restrict__ bias,
     const typename DT::storage* __restrict__ B_stack, const float* __restrict__ vpart,
@@ -795,6 +808,7 @@ __global__ __launch_bounds__(kWideThreads) void linear_wide_kernel(
     using T = typename DT::storage;
     using Ops = MfmaOps<DT>;
     using BOps = MfmaOps<BF16>;
+    constexpr int NT = WS::kNT, TN = WS::TN, WN = WS::WN, PD = WS::PD;
     constexpr int KQ = WideTerms<DT>::kK;
     constexpr int VQ = KQ + 8;  // padded row of V' (bank spread of the operand reads)
     constexpr bool kSplitB = std::is_same<DT, F16>::value;
@@ -804,8 +818,8 @@ __global__ __launch_bounds__(kWideThreads) void linear_wide_kernel(
                   "V' and B' fit the buffers");
     static_assert((KQ / 2) % 8 == 0, "an operand's 8 rows of B' lie in one stage");
     __shared__ __attribute__((aligned(16))) float s_v[kWideBM * kWideRG];
-    __shared__ int s_seg[kWideSegLds + 1];
-    __shared__ int s_ids[kWideSegLds];
+    __shared__ int s_seg[WS::kSegLds + 1];
+    __shared__ int s_ids[WS::kSegLds];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -817,11 +831,11 @@ __global__ __launch_bounds__(kWideThreads) void linear_wide_kernel(
     const int m0 = (t / tiles_n) * kWideBM;
     const int n0 = (t % tiles_n) * kWideBN;
     const int nchunks = (H1 + kWideBK - 1) / kWideBK;
-    const int wr0 = (wid / kWideWN) * (16 * kWideTM);  // first tile row of this wave
-    const int wc0 = (wid % kWideWN) * (16 * kWideTN);  // first tile column of this wave
+    const int wr0 = (wid / WN) * (16 * kWideTM);  // first tile row of this wave
+    const int wc0 = (wid % WN) * (16 * TN);  // first tile column of this wave
 
     // The segment table when it fits LDS.
-    const bool seg_lds = S <= kWideSegLds;  // no table is read when S == 0
+    const bool seg_lds = S <= WS::kSegLds;  // no table is read when S == 0
     if (seg_lds && S > 0) {
         if (tid <= S) s_seg[tid] = seg_indptr[tid];
         if (tid < S) s_ids[tid] = adapter_ids[tid];
@@ -855,7 +869,7 @@ __global__ __launch_bounds__(kWideThreads) void linear_wide_kernel(
     }
     // The first pass of v (before the main loop, whose loads it overlaps).
     auto fill_v = [&](int g0) {
-        for (int e = tid; e < kWideBM * kWideRG; e += kWideThreads) {
+        for (int e = tid; e < kWideBM * kWideRG; e += NT) {
             const int il = e / kWideRG, k = e % kWideRG;
             float v = 0.f;
             if (m0 + il < M && g0 + k < r)
@@ -868,38 +882,38 @@ __global__ __launch_bounds__(kWideThreads) void linear_wide_kernel(
     // ---- base product ------------------------------------------------------
     // A chunk of one operand is 256 rows x 8 pieces of 16 bytes: 4 pieces
     // per thread.
-    constexpr int kP = kWideBM * (kWideBK / 8) / kWideThreads;
-    static_assert(kP * kWideThreads == kWideBM * (kWideBK / 8), "whole pieces per thread");
-    uint4 ring[2 * kP];  // one chunk: this thread's pieces of x rows, then of W rows
-    auto load_chunk = [&](int c) {
+    constexpr int kP = kWideBM * (kWideBK / 8) / NT;
+    static_assert(kP * NT == kWideBM * (kWideBK / 8), "whole pieces per thread");
+    // ring[d]: a chunk's pieces for this thread, x rows then W rows.
+    uint4 ring[PD][2 * kP];
+    auto load_chunk = [&](int c, uint4(&dst)[2 * kP]) {
         const int k0 = c * kWideBK;
 #pragma unroll
         for (int u = 0; u < kP; ++u) {
-            const int id = tid + u * kWideThreads;
+            const int id = tid + u * NT;
             const int row = id >> 3, gk = k0 + (id & 7) * 8;
-            ring[u] = (m0 + row < M && gk < H1) ? load16(x + (long long)(m0 + row) * H1 + gk)
-                                                : make_uint4(0, 0, 0, 0);
-            ring[kP + u] = (n0 + row < H2 && gk < H1)
-                               ? load16(W + (long long)(n0 + row) * H1 + gk)
-                               : make_uint4(0, 0, 0, 0);
+            dst[u] = (m0 + row < M && gk < H1) ? load16(x + (long long)(m0 + row) * H1 + gk)
+                                               : make_uint4(0, 0, 0, 0);
+            dst[kP + u] = (n0 + row < H2 && gk < H1) ? load16(W + (long long)(n0 + row) * H1 + gk)
+                                                     : make_uint4(0, 0, 0, 0);
         }
     };
-    auto store_chunk = [&](uint16_t* sx, uint16_t* sw) {
+    auto store_chunk = [&](uint16_t* sx, uint16_t* sw, const uint4(&src)[2 * kP]) {
 #pragma unroll
         for (int u = 0; u < kP; ++u) {
-            const int id = tid + u * kWideThreads;
+            const int id = tid + u * NT;
             const int row = id >> 3, p = id & 7;  // row < kWideBM: off < kWideHalf
             const int off = row * kWideBK + ((p ^ (row & 7)) << 3);
-            *reinterpret_cast<uint4*>(sx + off) = ring[u];
-            *reinterpret_cast<uint4*>(sw + off) = ring[kP + u];
+            *reinterpret_cast<uint4*>(sx + off) = src[u];
+            *reinterpret_cast<uint4*>(sw + off) = src[kP + u];
         }
     };
 
-    mf32x4 acc[kWideTM][kWideTN];
+    mf32x4 acc[kWideTM][TN];
 #pragma unroll
     for (int i = 0; i < kWideTM; ++i)
 #pragma unroll
-        for (int j = 0; j < kWideTN; ++j) acc[i][j] = mf32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < TN; ++j) acc[i][j] = mf32x4{0.f, 0.f, 0.f, 0.f};
 
     // One chunk: two K steps of 32, each the wave's 4 W blocks against its 8
     // x blocks.
@@ -908,19 +922,19 @@ __global__ __launch_bounds__(kWideThreads) void linear_wide_kernel(
             const int p = 4 * ks + lg;  // 16-byte piece of the 32-k step
             return *reinterpret_cast<const uint4*>(base + row * kWideBK + ((p ^ (row & 7)) << 3));
         };
-        uint4 b0[kWideTN], b1[kWideTN];
+        uint4 b0[TN], b1[TN];
 #pragma unroll
-        for (int j = 0; j < kWideTN; ++j) b0[j] = rd(sw, wc0 + 16 * j + lr, 0);
+        for (int j = 0; j < TN; ++j) b0[j] = rd(sw, wc0 + 16 * j + lr, 0);
         uint4 a = rd(sx, wr0 + lr, 0);
 #pragma unroll
         for (int i = 0; i < kWideTM; ++i) {
             const uint4 an = rd(sx, wr0 + 16 * ((i + 1) % kWideTM) + lr, i + 1 < kWideTM ? 0 : 1);
             if (i == kWideTM / 2) {
 #pragma unroll
-                for (int j = 0; j < kWideTN; ++j) b1[j] = rd(sw, wc0 + 16 * j + lr, 1);
+                for (int j = 0; j < TN; ++j) b1[j] = rd(sw, wc0 + 16 * j + lr, 1);
             }
 #pragma unroll
-            for (int j = 0; j < kWideTN; ++j) acc[i][j] = Ops::mma(b0[j], a, acc[i][j]);
+            for (int j = 0; j < TN; ++j) acc[i][j] = Ops::mma(b0[j], a, acc[i][j]);
             a = an;
         }
 #pragma unroll
@@ -928,23 +942,28 @@ __global__ __launch_bounds__(kWideThreads) void linear_wide_kernel(
             uint4 an = a;
             if (i + 1 < kWideTM) an = rd(sx, wr0 + 16 * (i + 1) + lr, 1);
 #pragma unroll
-            for (int j = 0; j < kWideTN; ++j) acc[i][j] = Ops::mma(b1[j], a, acc[i][j]);
+            for (int j = 0; j < TN; ++j) acc[i][j] = Ops::mma(b1[j], a, acc[i][j]);
             a = an;
         }
     };
-    // Chunk c: its registers into buffer c % 2 (every wave is past the
-    // barrier of chunk c - 1, so done with chunk c - 2 there), the next
-    // chunk's loads issued, then the barrier and the MFMAs.
-    auto chunk = [&](int c, uint16_t* sx, uint16_t* sw) {
-        store_chunk(sx, sw);
-        if (c + 1 < nchunks) load_chunk(c + 1);
+    // Chunk c (parity P): its registers (ring slot c % PD) into buffer P
+    // (every wave is past the barrier of chunk c - 1, so done with chunk
+    // c - 2 there), chunk c + PD's loads issued into the freed slot, then the
+    // barrier and the MFMAs.
+    static_assert(PD == 1 || PD == 2, "ring slot c % PD has the parity's index");
+    auto chunk = [&](auto parity, int c, uint16_t* sx, uint16_t* sw) {
+        constexpr int P = decltype(parity)::value;
+        store_chunk(sx, sw, ring[P % PD]);
+        if (c + PD < nchunks) load_chunk(c + PD, ring[P % PD]);
         lds_barrier();
         compute(sx, sw);
     };
-    load_chunk(0);
+    load_chunk(0, ring[0]);
+    if constexpr (PD == 2)
+        if (1 < nchunks) load_chunk(1, ring[1 % PD]);
     for (int c = 0; c < nchunks; c += 2) {
-        chunk(c, s_wide0, s_wide1);
-        if (c + 1 < nchunks) chunk(c + 1, s_wide2, s_wide3);
+        chunk(std::integral_constant<int, 0>{}, c, s_wide0, s_wide1);
+        if (c + 1 < nchunks) chunk(std::integral_constant<int, 1>{}, c + 1, s_wide2, s_wide3);
     }
 
     // ---- correction ---------------------------------------------------------
@@ -954,16 +973,24 @@ __global__ __launch_bounds__(kWideThreads) void linear_wide_kernel(
     auto bq_row = [&](int k) {  // row k of B'
         return k < KQ / 2 ? s_wide2 + k * kWideLdB : s_wide3 + (k - KQ / 2) * kWideLdB;
     };
-    // This thread's piece of a B' pass: rank tid / 32, columns (tid % 32) * 8.
-    const int bk = tid >> 5, bc = n0 + (tid & 31) * 8;
+    // This thread's pieces of a B' pass (16 ranks x 32 pieces of 8 columns):
+    // piece q is rank (tid + q NT) / 32, columns ((tid + q NT) % 32) * 8.
+    constexpr int kBP = kWideRG * 32 / NT;
+    static_assert(kBP * NT == kWideRG * 32, "whole pieces per thread");
+    uint4 braw[kBP];
     auto load_b = [&](int s, int g0) {
         const int a = id_at(s);
-        return (g0 + bk < r && bc < H2)
-                   ? load16(B_stack + ((long long)a * r + g0 + bk) * H2 + bc)
-                   : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < kBP; ++q) {
+            const int id = tid + q * NT;
+            const int bk = id >> 5, bc = n0 + (id & 31) * 8;
+            braw[q] = (g0 + bk < r && bc < H2)
+                          ? load16(B_stack + ((long long)a * r + g0 + bk) * H2 + bc)
+                          : make_uint4(0, 0, 0, 0);
+        }
     };
     int seg_cur = next_segment(first);
-    uint4 braw = seg_cur < S ? load_b(seg_cur, 0) : make_uint4(0, 0, 0, 0);
+    if (seg_cur < S) load_b(seg_cur, 0);
     for (int g0 = 0; g0 < r && seg_cur < S; g0 += kWideRG) {
         // The stages (and, from the second pass, s_v) are free: every wave is
         // past its last step and, by the barrier's fence (vmcnt(0)), its
@@ -974,7 +1001,7 @@ __global__ __launch_bounds__(kWideThreads) void linear_wide_kernel(
             __syncthreads();
         }
         // V' rows: the terms of s v in the slot order of B'.
-        for (int e = tid; e < kWideBM * kWideRG; e += kWideThreads) {
+        for (int e = tid; e < kWideBM * kWideRG; e += NT) {
             const int il = e / kWideRG, k = e % kWideRG;
             const float v = scale * s_v[e];
             const uint32_t vh = BF16::f2b(v);
@@ -993,12 +1020,15 @@ __global__ __launch_bounds__(kWideThreads) void linear_wide_kernel(
                 q[3 * kWideRG + k] = 0;
             }
         }
-        if (g0 > 0) braw = load_b(seg_cur, g0);
+        if (g0 > 0) load_b(seg_cur, g0);
         while (seg_cur < S) {
             __syncthreads();  // V' written; the previous segment's reads of B' done
-            {
+#pragma unroll
+            for (int q = 0; q < kBP; ++q) {
+                const int id = tid + q * NT;
+                const int bk = id >> 5, c8 = (id & 31) * 8;
                 float f[8];
-                DT::unpack(braw, f);
+                DT::unpack(braw[q], f);
                 uint4 hi, lo;
                 if constexpr (kSplitB) {
                     uint32_t h[8], l[8];
@@ -1012,10 +1042,9 @@ __global__ __launch_bounds__(kWideThreads) void linear_wide_kernel(
                     lo = make_uint4(l[0] | l[1] << 16, l[2] | l[3] << 16, l[4] | l[5] << 16,
                                     l[6] | l[7] << 16);
                 } else {
-                    hi = braw;
+                    hi = braw[q];
                     lo = make_uint4(0, 0, 0, 0);
                 }
-                const int c8 = (tid & 31) * 8;
                 store16(bq_row(bk) + c8, hi);
                 store16(bq_row(kWideRG + bk) + c8, hi);
                 store16(bq_row(2 * kWideRG + bk) + c8, hi);
@@ -1031,16 +1060,16 @@ __global__ __launch_bounds__(kWideThreads) void linear_wide_kernel(
             const int lo_row = max(seg_at(seg_cur), m0);
             const int hi_row = min(seg_at(seg_cur + 1), row_end);
             const int seg_next = next_segment(seg_cur + 1);
-            if (seg_next < S) braw = load_b(seg_next, g0);  // in flight during the MFMAs
+            if (seg_next < S) load_b(seg_next, g0);  // in flight during the MFMAs
 #pragma unroll
             for (int ks = 0; ks < KQ / 32; ++ks) {
                 // this lane group's 8 rows of B' (one stage holds all of them)
                 const int k0 = ks * 32 + lg * 8;
                 const uint16_t* bbase = k0 < KQ / 2 ? s_wide2 : s_wide3;
                 const int kl = k0 < KQ / 2 ? k0 : k0 - KQ / 2;
-                uint4 bb[kWideTN];
+                uint4 bb[TN];
 #pragma unroll
-                for (int j = 0; j < kWideTN; ++j)
+                for (int j = 0; j < TN; ++j)
                     bb[j] = lds_operand_tr(bbase + wc0 + 16 * j, kl, kWideLdB, lr);
 #pragma unroll
                 for (int i = 0; i < kWideTM; ++i) {
@@ -1052,7 +1081,7 @@ __global__ __launch_bounds__(kWideThreads) void linear_wide_kernel(
                                                vq_row(wr0 + 16 * i + lr) + ks * 32 + lg * 8)
                                          : make_uint4(0, 0, 0, 0);
 #pragma unroll
-                    for (int j = 0; j < kWideTN; ++j) acc[i][j] = BOps::mma(bb[j], vv, acc[i][j]);
+                    for (int j = 0; j < TN; ++j) acc[i][j] = BOps::mma(bb[j], vv, acc[i][j]);
                 }
             }
             seg_cur = seg_next;
@@ -1063,7 +1092,7 @@ __global__ __launch_bounds__(kWideThreads) void linear_wide_kernel(
 
     // ---- bias, one rounding, store ------------------------------------------
 #pragma unroll
-    for (int j = 0; j < kWideTN; ++j) {
+    for (int j = 0; j < TN; ++j) {
         const int col = n0 + wc0 + 16 * j + 4 * lg;
         if (col >= H2) continue;
         float bv[4] = {0.f, 0.f, 0.f, 0.f};
