@@ -263,14 +263,16 @@ def test_wide_tiles_every_element(case):
     assert np.array_equal(_gpu_linear(w, W, b, d), got)
 
 
-def test_wide_tiles_integer_inputs_bit_for_bit():
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_wide_tiles_integer_inputs_bit_for_bit(dtype):
     """Exact integers through the 256 x 256 tiles: the correction's bf16
-    terms of v and of the fp16 weights add up exactly, so y must equal the
-    oracle's value bit for bit."""
-    w = wl.integer_exact(11, "f16", 64, 4096, 16, 5, 2048, 6, density=0.2, scale=2.0)
-    W, b = wl.base_layer(11, "f16", 64, 4096, integer=True, density=0.2)
+    terms of v (and, for fp16, of the weights) add up exactly, so y must
+    equal the oracle's value bit for bit."""
+    w = wl.integer_exact(11, dtype, 64, 4096, 16, 5, 2048, 6, density=0.2, scale=2.0)
+    W, b = wl.base_layer(11, dtype, 64, 4096, integer=True, density=0.2)
     ref = _oracle(w, W, b)
-    assert np.abs(ref).max() <= 2048, "inputs leave the exactly representable range"
+    limit = 2048 if dtype == "f16" else 256
+    assert np.abs(ref).max() <= limit, "inputs leave the exactly representable range"
     assert np.array_equal(_gpu_linear(w, W, b), ref)
 
 
@@ -313,16 +315,20 @@ def test_repeated_calls_are_bitwise_identical():
         assert np.array_equal(_gpu_linear(w, W, b, d), first)
 
 
-def test_graph_replay_matches_eager():
+# (rows, H1, H2, segments): decode tiles with the shrink folded in, and the
+# 256 x 256 tiles after the mixed shrink launch.
+@pytest.mark.parametrize("R,H1,H2,S", [(48, 512, 256, 12), (2048, 128, 4096, 8)],
+                         ids=["decode_tiles", "wide_tiles"])
+def test_graph_replay_matches_eager(R, H1, H2, S):
     import torch
     import segmented_gather_gemv_sgmv_amd as sg
-    w = wl.small_random(16, "bf16", 512, 256, 16, 8, 48, 12)
-    W, b = wl.base_layer(16, "bf16", 512, 256)
+    w = wl.small_random(16, "bf16", H1, H2, 16, 8, R, S)
+    W, b = wl.base_layer(16, "bf16", H1, H2)
     d = to_device(w)
     Wd, bd = _dev(W, "bf16"), _dev(b, "bf16")
-    need = sg.lora_linear_workspace_bytes(48, 12, 512, 256, 16, torch.bfloat16)
+    need = sg.lora_linear_workspace_bytes(R, S, H1, H2, 16, torch.bfloat16)
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
-    out = torch.empty((48, 256), dtype=torch.bfloat16, device="cuda:0")
+    out = torch.empty((R, H2), dtype=torch.bfloat16, device="cuda:0")
     sg.lora_linear(d["x"], Wd, d["A"], d["B"], d["seg"], d["ids"], w.scale, bias=bd, out=out,
                    workspace=ws)
     torch.cuda.synchronize()
