@@ -246,6 +246,7 @@ WIDE_CASES = [
     (42, "bf16", 256, 4096, 16, 6, 2048, 16, 0, True),  # bf16
     (43, "f16", 128, 2048, 40, 5, 4096, 24, 0, False),  # rank passes 16 + 16 + 8, no bias
     (44, "bf16", 128, 4096, 128, 3, 2100, 4, 30, True),  # r = 128, uncovered tail rows
+    (46, "f16", 64, 2048, 16, 8, 16640, 520, 0, True),   # table past LDS (520 segments)
 ]
 
 
