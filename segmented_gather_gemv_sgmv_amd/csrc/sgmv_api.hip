@@ -1592,12 +1592,16 @@ int lora_linear(void* y, const void* x, const void* W, const void* bias, const v
                 return;
             }
             if (tiled) {
-                if (lp.cfg == 2)
-                    launch(&linear_wide_kernel<DT, LinWide>, dim3((unsigned)lp.tiles),
-                           dim3(LinWide::kNT), st, (T*)y, (const T*)x, (const T*)W,
-                           (const T*)bias, (const T*)B_stack, (const float*)vpart, vstride,
-                           vsplit, seg_indptr, adapter_ids, num_segments, num_rows, num_adapters,
-                           H1, H2, r, scale, (int)lp.tiles_n, (int)lp.tiles);
+                if (lp.cfg == 2) {
+                    // direct global-to-LDS stages when K is whole steps of 4 x 32
+                    auto k = H1 % 128 == 0 ? &linear_wide_kernel<DT, LinWide, true>
+                                           : &linear_wide_kernel<DT, LinWide, false>;
+                    launch(k, dim3((unsigned)lp.tiles), dim3(LinWide::kNT), st, (T*)y,
+                           (const T*)x, (const T*)W, (const T*)bias, (const T*)B_stack,
+                           (const float*)vpart, vstride, vsplit, seg_indptr, adapter_ids,
+                           num_segments, num_rows, num_adapters, H1, H2, r, scale,
+                           (int)lp.tiles_n, (int)lp.tiles);
+                }
                 else if (lp.cfg == 0)
                     launch_linear_tiled<DT, LinSkinny>(y, x, W, bias, B_stack, vpart, vstride,
                                                        vsplit, seg_indptr, adapter_ids,

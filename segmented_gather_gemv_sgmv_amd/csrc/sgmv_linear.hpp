@@ -749,6 +749,7 @@ constexpr int kWideTM = 8;                         // 16-row blocks per wave: 12
 constexpr int kWideBK = 64;                        // K per chunk
 constexpr int kWideHalf = kWideBM * kWideBK;       // 16-bit elements of one operand's chunk
 constexpr int kWideRG = 16;                        // ranks per correction pass
+constexpr int kWideStages = 4;                     // direct-load stages of 32 K
 constexpr int kWideLdB = kWideBN + 16;  // padded row of B' (transposing reads)
 static_assert(kWideBM == kWideBN, "square tile");
 
@@ -786,6 +787,15 @@ __shared__ __attribute__((aligned(16))) uint16_t s_wide1[kWideHalf];
 __shared__ __attribute__((aligned(16))) uint16_t s_wide2[kWideHalf];
 __shared__ __attribute__((aligned(16))) uint16_t s_wide3[kWideHalf];
 
+// The four LDS arrays by index (compile time), for the direct-load stages.
+template <int B>
+__device__ __forceinline__ uint16_t* wide_stage() {
+    if constexpr (B == 0) return s_wide0;
+    else if constexpr (B == 1) return s_wide1;
+    else if constexpr (B == 2) return s_wide2;
+    else return s_wide3;
+}
+
 // bf16 terms of a float: hi, and the rounded remainder (0 for inf / NaN,
 // whose remainder is not a number).
 __device__ __forceinline__ uint32_t bf16_rest(float f, uint32_t hi) {
@@ -797,7 +807,7 @@ __device__ __forceinline__ uint32_t bf16_rest(float f, uint32_t hi) {
 // (whole rows of tiles at the usual shapes), so its L2 serves the x rows
 // those tiles share.  H1 and H2 are multiples of 8; x, W, y and bias are
 // 16-byte aligned.
-template <typename DT, typename WS>
+template <typename DT, typename WS, bool kDma>
 __global__ __launch_bounds__(WS::kNT) void linear_wide_kernel(
     typename DT::storage* __restrict__ y, const typename DT::storage* __restrict__ x,
     const typename DT::storage* __restrict__ W, const typename DT::storage* __restrict__ bias,
@@ -880,90 +890,163 @@ __global__ __launch_bounds__(WS::kNT) void linear_wide_kernel(
     if (next_segment(first) < S) fill_v(0);  // uniform; tiles without adapted rows skip it
 
     // ---- base product ------------------------------------------------------
-    // A chunk of one operand is 256 rows x 8 pieces of 16 bytes: 4 pieces
-    // per thread.
-    constexpr int kP = kWideBM * (kWideBK / 8) / NT;
-    static_assert(kP * NT == kWideBM * (kWideBK / 8), "whole pieces per thread");
-    // ring[d]: a chunk's pieces for this thread, x rows then W rows.
-    uint4 ring[PD][2 * kP];
-    auto load_chunk = [&](int c, uint4(&dst)[2 * kP]) {
-        const int k0 = c * kWideBK;
-#pragma unroll
-        for (int u = 0; u < kP; ++u) {
-            const int id = tid + u * NT;
-            const int row = id >> 3, gk = k0 + (id & 7) * 8;
-            dst[u] = (m0 + row < M && gk < H1) ? load16(x + (long long)(m0 + row) * H1 + gk)
-                                               : make_uint4(0, 0, 0, 0);
-            dst[kP + u] = (n0 + row < H2 && gk < H1) ? load16(W + (long long)(n0 + row) * H1 + gk)
-                                                     : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto store_chunk = [&](uint16_t* sx, uint16_t* sw, const uint4(&src)[2 * kP]) {
-#pragma unroll
-        for (int u = 0; u < kP; ++u) {
-            const int id = tid + u * NT;
-            const int row = id >> 3, p = id & 7;  // row < kWideBM: off < kWideHalf
-            const int off = row * kWideBK + ((p ^ (row & 7)) << 3);
-            *reinterpret_cast<uint4*>(sx + off) = src[u];
-            *reinterpret_cast<uint4*>(sw + off) = src[kP + u];
-        }
-    };
-
     mf32x4 acc[kWideTM][TN];
 #pragma unroll
     for (int i = 0; i < kWideTM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = mf32x4{0.f, 0.f, 0.f, 0.f};
-
-    // One chunk: two K steps of 32, each the wave's 4 W blocks against its 8
-    // x blocks.
-    auto compute = [&](const uint16_t* sx, const uint16_t* sw) {
-        auto rd = [&](const uint16_t* base, int row, int ks) {
-            const int p = 4 * ks + lg;  // 16-byte piece of the 32-k step
-            return *reinterpret_cast<const uint4*>(base + row * kWideBK + ((p ^ (row & 7)) << 3));
+    if constexpr (kDma) {
+        // Steps of 32 K through four stages (s_wide0..3: 256 rows of x then
+        // 256 rows of W, 64 bytes each), filled by direct global-to-LDS loads
+        // three steps ahead: global_load_lds_dwordx4 writes lane i's 16 bytes
+        // at the wave's LDS base + 16 i, so wave w fills stage rows
+        // [64 w, 64 w + 64) with four loads of 16 rows, each lane fetching the
+        // piece its slot holds (piece p of row r sits at slot
+        // p ^ ((r >> 1) & 3)).  Rows past M or H2 read the last valid row
+        // (their results are never stored).  Step c waits for its own loads
+        // (the later two steps' stay in flight) and for its LDS reads of step
+        // c - 1, then for every wave; after that barrier stage (c + 3) % 4,
+        // read in step c - 1, takes step c + 3.  Every step issues loads (past
+        // the last step they re-read it into a stage no step reads) and the
+        // loop has no early exit, H1 being a multiple of 128: with a path-
+        // independent count of later loads the compiler adds no wait of its
+        // own before a stage's reads (each stage is an LDS array of its own,
+        // so it can tell the stages apart).
+        const int nsteps = H1 / 32;
+        const int lrow = lane >> 2;
+        using lds_t = __attribute__((address_space(3))) void;
+        const T* gsrc[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int row = 64 * wid + 16 * u + lrow;
+            const int piece = (lane & 3) ^ ((row >> 1) & 3);
+            gsrc[u] = row < kWideBM
+                          ? x + (long long)min(m0 + row, M - 1) * H1 + piece * 8
+                          : W + (long long)min(n0 + row - kWideBM, H2 - 1) * H1 + piece * 8;
+        }
+        auto issue = [&](uint16_t* st, int step) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                __builtin_amdgcn_global_load_lds((const void*)(gsrc[u] + step * 32),
+                                                 (lds_t*)(st + (64 * wid + 16 * u) * 32), 16, 0,
+                                                 0);
         };
-        uint4 b0[TN], b1[TN];
+        auto compute = [&](const uint16_t* st) {
+            auto rd = [&](int row) {
+                return *reinterpret_cast<const uint4*>(st + row * 32 +
+                                                       ((lg ^ ((row >> 1) & 3)) << 3));
+            };
+            uint4 b[TN];
 #pragma unroll
-        for (int j = 0; j < TN; ++j) b0[j] = rd(sw, wc0 + 16 * j + lr, 0);
-        uint4 a = rd(sx, wr0 + lr, 0);
+            for (int j = 0; j < TN; ++j) b[j] = rd(kWideBM + wc0 + 16 * j + lr);
 #pragma unroll
-        for (int i = 0; i < kWideTM; ++i) {
-            const uint4 an = rd(sx, wr0 + 16 * ((i + 1) % kWideTM) + lr, i + 1 < kWideTM ? 0 : 1);
-            if (i == kWideTM / 2) {
+            for (int i = 0; i < kWideTM; ++i) {
+                const uint4 a = rd(wr0 + 16 * i + lr);
 #pragma unroll
-                for (int j = 0; j < TN; ++j) b1[j] = rd(sw, wc0 + 16 * j + lr, 1);
+                for (int j = 0; j < TN; ++j) acc[i][j] = Ops::mma(b[j], a, acc[i][j]);
             }
-#pragma unroll
-            for (int j = 0; j < TN; ++j) acc[i][j] = Ops::mma(b0[j], a, acc[i][j]);
-            a = an;
+        };
+        auto step = [&](auto stage_c, int c) {
+            constexpr int B = decltype(stage_c)::value;
+            __builtin_amdgcn_s_waitcnt(0x0078);  // vmcnt(8), lgkmcnt(0)
+            asm volatile("" ::: "memory");       // no LDS access moves across the barrier
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            issue(wide_stage<(B + 3) & 3>(), min(c + 3, nsteps - 1));
+            compute(wide_stage<B>());
+        };
+        static_assert(kWideStages == 4, "four stages");
+        issue(wide_stage<0>(), 0);
+        issue(wide_stage<1>(), min(1, nsteps - 1));
+        issue(wide_stage<2>(), min(2, nsteps - 1));
+        for (int c0 = 0; c0 < nsteps; c0 += 4) {
+            step(std::integral_constant<int, 0>{}, c0);
+            step(std::integral_constant<int, 1>{}, c0 + 1);
+            step(std::integral_constant<int, 2>{}, c0 + 2);
+            step(std::integral_constant<int, 3>{}, c0 + 3);
         }
-#pragma unroll
-        for (int i = 0; i < kWideTM; ++i) {
-            uint4 an = a;
-            if (i + 1 < kWideTM) an = rd(sx, wr0 + 16 * (i + 1) + lr, 1);
-#pragma unroll
-            for (int j = 0; j < TN; ++j) acc[i][j] = Ops::mma(b1[j], a, acc[i][j]);
-            a = an;
+        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0): the stages are quiet
+    } else {
+        // A chunk of one operand is 256 rows x 8 pieces of 16 bytes: 4 pieces
+        // per thread.
+        constexpr int kP = kWideBM * (kWideBK / 8) / NT;
+        static_assert(kP * NT == kWideBM * (kWideBK / 8), "whole pieces per thread");
+        // ring[d]: a chunk's pieces for this thread, x rows then W rows.
+        uint4 ring[PD][2 * kP];
+        auto load_chunk = [&](int c, uint4(&dst)[2 * kP]) {
+            const int k0 = c * kWideBK;
+    #pragma unroll
+            for (int u = 0; u < kP; ++u) {
+                const int id = tid + u * NT;
+                const int row = id >> 3, gk = k0 + (id & 7) * 8;
+                dst[u] = (m0 + row < M && gk < H1) ? load16(x + (long long)(m0 + row) * H1 + gk)
+                                                   : make_uint4(0, 0, 0, 0);
+                dst[kP + u] = (n0 + row < H2 && gk < H1) ? load16(W + (long long)(n0 + row) * H1 + gk)
+                                                         : make_uint4(0, 0, 0, 0);
+            }
+        };
+        auto store_chunk = [&](uint16_t* sx, uint16_t* sw, const uint4(&src)[2 * kP]) {
+    #pragma unroll
+            for (int u = 0; u < kP; ++u) {
+                const int id = tid + u * NT;
+                const int row = id >> 3, p = id & 7;  // row < kWideBM: off < kWideHalf
+                const int off = row * kWideBK + ((p ^ (row & 7)) << 3);
+                *reinterpret_cast<uint4*>(sx + off) = src[u];
+                *reinterpret_cast<uint4*>(sw + off) = src[kP + u];
+            }
+        };
+
+
+        // One chunk: two K steps of 32, each the wave's 4 W blocks against its 8
+        // x blocks.
+        auto compute = [&](const uint16_t* sx, const uint16_t* sw) {
+            auto rd = [&](const uint16_t* base, int row, int ks) {
+                const int p = 4 * ks + lg;  // 16-byte piece of the 32-k step
+                return *reinterpret_cast<const uint4*>(base + row * kWideBK + ((p ^ (row & 7)) << 3));
+            };
+            uint4 b0[TN], b1[TN];
+    #pragma unroll
+            for (int j = 0; j < TN; ++j) b0[j] = rd(sw, wc0 + 16 * j + lr, 0);
+            uint4 a = rd(sx, wr0 + lr, 0);
+    #pragma unroll
+            for (int i = 0; i < kWideTM; ++i) {
+                const uint4 an = rd(sx, wr0 + 16 * ((i + 1) % kWideTM) + lr, i + 1 < kWideTM ? 0 : 1);
+                if (i == kWideTM / 2) {
+    #pragma unroll
+                    for (int j = 0; j < TN; ++j) b1[j] = rd(sw, wc0 + 16 * j + lr, 1);
+                }
+    #pragma unroll
+                for (int j = 0; j < TN; ++j) acc[i][j] = Ops::mma(b0[j], a, acc[i][j]);
+                a = an;
+            }
+    #pragma unroll
+            for (int i = 0; i < kWideTM; ++i) {
+                uint4 an = a;
+                if (i + 1 < kWideTM) an = rd(sx, wr0 + 16 * (i + 1) + lr, 1);
+    #pragma unroll
+                for (int j = 0; j < TN; ++j) acc[i][j] = Ops::mma(b1[j], a, acc[i][j]);
+                a = an;
+            }
+        };
+        // Chunk c (parity P): its registers (ring slot c % PD) into buffer P
+        // (every wave is past the barrier of chunk c - 1, so done with chunk
+        // c - 2 there), chunk c + PD's loads issued into the freed slot, then the
+        // barrier and the MFMAs.
+        static_assert(PD == 1 || PD == 2, "ring slot c % PD has the parity's index");
+        auto chunk = [&](auto parity, int c, uint16_t* sx, uint16_t* sw) {
+            constexpr int P = decltype(parity)::value;
+            store_chunk(sx, sw, ring[P % PD]);
+            if (c + PD < nchunks) load_chunk(c + PD, ring[P % PD]);
+            lds_barrier();
+            compute(sx, sw);
+        };
+        load_chunk(0, ring[0]);
+        if constexpr (PD == 2)
+            if (1 < nchunks) load_chunk(1, ring[1 % PD]);
+        for (int c = 0; c < nchunks; c += 2) {
+            chunk(std::integral_constant<int, 0>{}, c, s_wide0, s_wide1);
+            if (c + 1 < nchunks) chunk(std::integral_constant<int, 1>{}, c + 1, s_wide2, s_wide3);
         }
-    };
-    // Chunk c (parity P): its registers (ring slot c % PD) into buffer P
-    // (every wave is past the barrier of chunk c - 1, so done with chunk
-    // c - 2 there), chunk c + PD's loads issued into the freed slot, then the
-    // barrier and the MFMAs.
-    static_assert(PD == 1 || PD == 2, "ring slot c % PD has the parity's index");
-    auto chunk = [&](auto parity, int c, uint16_t* sx, uint16_t* sw) {
-        constexpr int P = decltype(parity)::value;
-        store_chunk(sx, sw, ring[P % PD]);
-        if (c + PD < nchunks) load_chunk(c + PD, ring[P % PD]);
-        lds_barrier();
-        compute(sx, sw);
-    };
-    load_chunk(0, ring[0]);
-    if constexpr (PD == 2)
-        if (1 < nchunks) load_chunk(1, ring[1 % PD]);
-    for (int c = 0; c < nchunks; c += 2) {
-        chunk(std::integral_constant<int, 0>{}, c, s_wide0, s_wide1);
-        if (c + 1 < nchunks) chunk(std::integral_constant<int, 1>{}, c + 1, s_wide2, s_wide3);
     }
 
     // ---- correction ---------------------------------------------------------
