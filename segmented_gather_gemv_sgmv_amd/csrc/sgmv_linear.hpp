@@ -900,7 +900,7 @@ __global__ __launch_bounds__(WS::kNT) void linear_wide_kernel(
         // 256 rows of W, 64 bytes each), filled by direct global-to-LDS loads
         // three steps ahead: global_load_lds_dwordx4 writes lane i's 16 bytes
         // at the wave's LDS base + 16 i, so wave w fills stage rows
-        // [64 w, 64 w + 64) with four loads of 16 rows, each lane fetching the
+        // [kRowsW w, kRowsW (w + 1)) with loads of 16 rows, each lane fetching the
         // piece its slot holds (piece p of row r sits at slot
         // p ^ ((r >> 1) & 3)).  Rows past M or H2 read the last valid row
         // (their results are never stored).  Step c waits for its own loads
@@ -915,10 +915,17 @@ __global__ __launch_bounds__(WS::kNT) void linear_wide_kernel(
         const int nsteps = H1 / 32;
         const int lrow = lane >> 2;
         using lds_t = __attribute__((address_space(3))) void;
-        const T* gsrc[4];
+        // kRowsW stage rows per wave in kLoadsW loads of 16 rows (64 rows and
+        // 4 loads with eight waves).
+        constexpr int kRowsW = 2 * kWideBM / (NT / kWave);
+        constexpr int kLoadsW = kRowsW / 16;
+        static_assert(kLoadsW * 16 * (NT / kWave) == 2 * kWideBM, "whole loads per wave");
+        static_assert(2 * kLoadsW < 64, "the wait count fits vmcnt");
+        constexpr int kWaitSteps = (2 * kLoadsW & 15) | ((2 * kLoadsW >> 4) << 14) | 0x0070;
+        const T* gsrc[kLoadsW];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int row = 64 * wid + 16 * u + lrow;
+        for (int u = 0; u < kLoadsW; ++u) {
+            const int row = kRowsW * wid + 16 * u + lrow;
             const int piece = (lane & 3) ^ ((row >> 1) & 3);
             gsrc[u] = row < kWideBM
                           ? x + (long long)min(m0 + row, M - 1) * H1 + piece * 8
@@ -926,10 +933,10 @@ __global__ __launch_bounds__(WS::kNT) void linear_wide_kernel(
         }
         auto issue = [&](uint16_t* st, int step) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int u = 0; u < kLoadsW; ++u)
                 __builtin_amdgcn_global_load_lds((const void*)(gsrc[u] + step * 32),
-                                                 (lds_t*)(st + (64 * wid + 16 * u) * 32), 16, 0,
-                                                 0);
+                                                 (lds_t*)(st + (kRowsW * wid + 16 * u) * 32), 16,
+                                                 0, 0);
         };
         auto compute = [&](const uint16_t* st) {
             auto rd = [&](int row) {
@@ -948,7 +955,7 @@ __global__ __launch_bounds__(WS::kNT) void linear_wide_kernel(
         };
         auto step = [&](auto stage_c, int c) {
             constexpr int B = decltype(stage_c)::value;
-            __builtin_amdgcn_s_waitcnt(0x0078);  // vmcnt(8), lgkmcnt(0)
+            __builtin_amdgcn_s_waitcnt(kWaitSteps);  // vmcnt(two steps' loads), lgkmcnt(0)
             asm volatile("" ::: "memory");       // no LDS access moves across the barrier
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
