@@ -754,7 +754,6 @@ __global__ __launch_bounds__(kMixedThreads, 4) void lora_mixed_kernel(
     float scale, float* __restrict__ partials, int* __restrict__ counters, MixedSplit sp,
     int n_counters, int counter_stride, long long wait_ticks, int guess) {
     using C = MixedClasses<LP, SP, GP>;
-    constexpr int NW = kMixedThreads / kWave;
     __shared__ __align__(16) unsigned char s_mem[C::kLdsBytes];
     __shared__ int s_scan[kMixedScanInts];
     // guess: a table shape the host expects, so that a shrink item streams
@@ -902,7 +901,6 @@ __global__ __launch_bounds__(kMixedThreads, R <= 32 ? 6 : (R == 64 ? 5 : 1)) voi
     float* __restrict__ v_final, int* __restrict__ counters, int counter_stride,
     int4* __restrict__ items, int n_items_max) {
     using C = MixedClasses<LP, SP, GP>;
-    constexpr int NW = kMixedThreads / kWave;
     __shared__ __align__(16) unsigned char s_mem[C::kLdsBytes];
     __shared__ int s_scan[kMixedScanInts];
     __shared__ int s_last;
@@ -951,7 +949,6 @@ __global__ __launch_bounds__(kMixedThreads, R >= 64 ? 4 : 5) void expand_mixed_k
     int num_adapters, int H2, float scale, const float* __restrict__ partials, MixedSplit sp,
     int P_long, int P_short, int P_single, const int4* __restrict__ items, int n_items_max) {
     using C = MixedClasses<LP, SP, GP>;
-    constexpr int NW = kMixedThreads / kWave;
     __shared__ __align__(16) unsigned char s_mem[C::kLdsBytes];
     __shared__ int s_scan[kMixedScanInts];
     Tile t;
