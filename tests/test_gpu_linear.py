@@ -239,7 +239,8 @@ def test_prefill_tiling_every_row():
 
 
 # 256 x 256 tiles (linear_wide_kernel): at least 128 tiles and segments of
-# 32 or more rows on average.  (seed, dtype, H1, H2, r, N, R, S, uncovered
+# 32 or more rows on average.  H1 a multiple of 128 takes the direct-load
+# stages (cases 42, 43, 44, 47), other H1 the register-staged chunks.  (seed, dtype, H1, H2, r, N, R, S, uncovered
 # tail, bias)
 WIDE_CASES = [
     (41, "f16", 264, 4088, 16, 8, 2000, 12, 7, True),   # ragged rows, columns, K chunk
@@ -247,6 +248,7 @@ WIDE_CASES = [
     (43, "f16", 128, 2048, 40, 5, 4096, 24, 0, False),  # rank passes 16 + 16 + 8, no bias
     (44, "bf16", 128, 4096, 128, 3, 2100, 4, 30, True),  # r = 128, uncovered tail rows
     (46, "f16", 64, 2048, 16, 8, 16640, 520, 0, True),   # table past LDS (520 segments)
+    (47, "bf16", 256, 4040, 32, 6, 2000, 10, 5, True),   # direct-load stages, ragged rows and columns
 ]
 
 
