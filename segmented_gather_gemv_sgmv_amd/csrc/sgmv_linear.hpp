@@ -723,11 +723,12 @@ __global__ __launch_bounds__(kLinThreads) void linear_lora_kernel(
 // rows of x and of W once.  A workgroup is one of the WideShape forms below:
 // eight waves of 128 rows x 64 columns, or four of 128 x 128.
 //
-// K moves in chunks of 64 through two LDS buffers (x rows in one array, W
-// rows in another, 32 KB each), loaded through registers one or two chunks
-// ahead.
-// In LDS each 128-byte row keeps its 16-byte piece p at p ^ (row & 7), which
-// spreads the rows an MFMA operand read touches over the banks.
+// K moves through four 32 KB LDS arrays.  When H1 is a multiple of 128 they
+// are four stages of 32 K filled by direct global-to-LDS loads three steps
+// ahead (kDma); otherwise they are two buffers of 64 K (x rows in one array,
+// W rows in the other), loaded through registers one chunk ahead.  In LDS a
+// row keeps its 16-byte pieces XOR-swizzled by its row index, which spreads
+// the rows an MFMA operand read touches over the banks.
 //
 // The product is computed transposed, Y^T = W X^T (W as the MFMA's A
 // operand), so that each lane's accumulator holds four consecutive columns
@@ -908,10 +909,15 @@ __global__ __launch_bounds__(WS::kNT) void linear_wide_kernel(
         // c - 1, then for every wave; after that barrier stage (c + 3) % 4,
         // read in step c - 1, takes step c + 3.  Every step issues loads (past
         // the last step they re-read it into a stage no step reads) and the
-        // loop has no early exit, H1 being a multiple of 128: with a path-
-        // independent count of later loads the compiler adds no wait of its
-        // own before a stage's reads (each stage is an LDS array of its own,
-        // so it can tell the stages apart).
+        // loop has no early exit, H1 being a multiple of 128.
+        //
+        // The compiler then adds no wait of its own for these loads before a
+        // stage's LDS reads, because it can tell the stages apart: each is
+        // an LDS array of its own; the count of later loads does not depend
+        // on the path; and the first load it records into a stage spans the
+        // whole stage in its offset range (wave w's first load sits at row
+        // kRowsW w).  Short of any of these it waits for every outstanding
+        // load (vmcnt(0)) before each step's first read.
         const int nsteps = H1 / 32;
         const int lrow = lane >> 2;
         using lds_t = __attribute__((address_space(3))) void;
